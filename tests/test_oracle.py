@@ -1,0 +1,324 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test checks one part of the oracle against the definition's closed forms,
+invariants, special cases that reduce to a library routine, brute force on tiny
+inputs, or numbers printed on the pages.  The selection covers the plausible
+mistakes: a dropped bias, a reversed sort or tie-break, a wrong softmax sign, an
+unstable or unpadded alignment, a transposed expert operand, gate and up
+swapped, the router weight applied to the wrong slot.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_decode_bf16_exhaustive_matches_torch():
+    codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    got = O.decode_bf16(codes)
+    same = (got == ref.astype(np.float64)) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+def test_decode_e4m3fn_exhaustive_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    got = O.decode_e4m3fn(codes)
+    same = (got == ref.astype(np.float64)) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+    # format facts: max finite 448, smallest subnormal 2^-9, NaN only at S.1111.111
+    assert np.nanmax(got) == 448.0
+    assert got[1] == 2.0 ** -9
+    assert np.isnan(got).sum() == 2
+
+
+# ---------------------------------------------------------------- router
+
+def _sorted_bruteforce(L, k):
+    out = []
+    for row in L:
+        order = sorted(range(len(row)), key=lambda e: (-row[e], e))
+        out.append(order[:k])
+    return np.array(out, np.int32)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (16, 1), (128, 8), (256, 8), (5, 5)])
+def test_select_topk_matches_bruteforce_sort(E, k):
+    rng = np.random.default_rng(E * 31 + k)
+    L = rng.standard_normal((64, E))
+    # inject exact ties, including across the k boundary
+    L[:, E // 2] = L[:, 0]
+    L[::3, -1] = L[::3, 1]
+    assert (O.select_topk(L, k) == _sorted_bruteforce(L, k)).all()
+
+
+def test_select_topk_ties_go_to_lower_index():
+    L = np.array([[0.5, 1.0, 1.0, 0.2, 1.0]])
+    assert O.select_topk(L, 2).tolist() == [[1, 2]]
+    assert O.select_topk(L, 4).tolist() == [[1, 2, 4, 0]]
+    assert O.select_topk(np.zeros((1, 6)), 3).tolist() == [[0, 1, 2]]
+
+
+def test_select_topk_k_equals_E_is_full_descending_argsort():
+    rng = np.random.default_rng(7)
+    L = rng.standard_normal((10, 9))
+    assert (O.select_topk(L, 9) == np.argsort(-L, axis=1)).all()
+
+
+def test_route_one_hot_bias_puts_that_expert_first():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((20, 16))
+    wr = rng.standard_normal((16, 8)) / 4
+    bias = np.zeros(8)
+    bias[5] = 1e4
+    _, ids, w = O.route(x, wr, bias, 2)
+    assert (ids[:, 0] == 5).all()
+    # the rest of the ranking is the unbiased ranking with expert 5 removed
+    _, ids0, _ = O.route(x, wr, None, 8)
+    for t in range(20):
+        rest = [e for e in ids0[t] if e != 5]
+        assert ids[t, 1] == rest[0]
+    assert np.allclose(w[:, 0], 1.0) and np.allclose(w[:, 1], 0.0, atol=1e-300)
+
+
+def test_topk_weights_closed_forms():
+    rng = np.random.default_rng(11)
+    L = rng.standard_normal((50, 12)) * 3
+    ids = O.select_topk(L, 4)
+    w = O.topk_weights(L, ids)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert (w > 0).all()
+    # descending slots carry non-increasing weights
+    assert (np.diff(w, axis=1) <= 1e-15).all()
+    # ratio of two slots = exp(logit difference) (softmax normalisation cancels)
+    r = w[:, 0] / w[:, 1]
+    d = np.take_along_axis(L, ids[:, :1], 1)[:, 0] - np.take_along_axis(L, ids[:, 1:2], 1)[:, 0]
+    assert np.allclose(r, np.exp(d), rtol=1e-12)
+    # shift invariance
+    assert np.allclose(O.topk_weights(L + 123.0, ids), w, rtol=1e-12)
+    # k = 1 -> weight exactly 1; equal logits -> 1/k
+    assert (O.topk_weights(L, O.select_topk(L, 1)) == 1.0).all()
+    Z = np.zeros((3, 8))
+    assert np.allclose(O.topk_weights(Z, O.select_topk(Z, 4)), 0.25, rtol=0, atol=1e-15)
+
+
+def test_topk_weights_worked_example():
+    # logits (ln 3, 0, ln 1/2, -inf-ish): top-2 = experts 0 and 1 with
+    # renormalised masses 3/(3+1) and 1/(3+1)
+    L = np.array([[math.log(3.0), 0.0, math.log(0.5), -40.0]])
+    ids = O.select_topk(L, 2)
+    assert ids.tolist() == [[0, 1]]
+    assert np.allclose(O.topk_weights(L, ids), [[0.75, 0.25]], rtol=0, atol=1e-15)
+    ids3 = O.select_topk(L, 3)
+    assert np.allclose(O.topk_weights(L, ids3), [[3 / 4.5, 1 / 4.5, 0.5 / 4.5]], atol=1e-15)
+
+
+def test_route_decides_in_given_precision():
+    # two logits that differ only below fp32 resolution tie in fp32 and so go to
+    # the lower index; in float64 the larger one wins
+    x = np.array([[1.0]])
+    wr = np.array([[1.0, 1.0 + 2.0 ** -40]])
+    _, ids32, _ = O.route(x, wr, None, 1, decision_dtype=np.float32)
+    _, ids64, _ = O.route(x, wr, None, 1, decision_dtype=None)
+    assert ids32.tolist() == [[0]] and ids64.tolist() == [[1]]
+
+
+# ---------------------------------------------------------------- alignment
+
+def test_align_hand_worked_example():
+    # 5 tokens, top-2, 4 experts, blocks of 4 rows.  Flat entries i = t*k + j:
+    #   i: 0 1 2 3 4 5 6 7 8 9
+    #   e: 2 0 0 2 3 2 2 1 0 3
+    # counts = [3, 1, 4, 2]; each pads to 4 -> offsets [0, 4, 8, 12, 16];
+    # capacity = 4 * floor((10 + 4*3) / 4) = 20 rows, i.e. one spare block.
+    ids = np.array([[2, 0], [0, 2], [3, 2], [2, 1], [0, 3]])
+    al = O.align(ids, 4, 4)
+    assert al["counts"].tolist() == [3, 1, 4, 2]
+    assert al["offsets"].tolist() == [0, 4, 8, 12, 16]
+    assert al["sorted_ids"].tolist() == [1, 2, 8, -1, 7, -1, -1, -1, 0, 3, 5, 6,
+                                         4, 9, -1, -1, -1, -1, -1, -1]
+    assert al["inv_pos"].tolist() == [8, 0, 1, 9, 12, 10, 11, 4, 2, 13]
+    assert al["block_expert"].tolist() == [0, 1, 2, 3, -1]
+
+
+def _check_alignment_invariants(ids, E, bm, al):
+    T, k = ids.shape
+    n = T * k
+    c, off, s, inv, be = (al[x] for x in ("counts", "offsets", "sorted_ids", "inv_pos", "block_expert"))
+    assert c.sum() == n
+    assert (c == np.bincount(ids.ravel(), minlength=E)).all()
+    assert off[0] == 0 and (off % bm == 0).all() and (np.diff(off) >= c).all()
+    assert (np.diff(off) - c < bm).all()
+    assert len(s) == O.capacity(T, E, k, bm) >= off[E]
+    real = s[s >= 0]
+    assert sorted(real.tolist()) == list(range(n))           # bijection
+    assert (s[inv] == np.arange(n)).all()
+    for e in range(E):
+        seg = s[off[e]:off[e + 1]]
+        assert (seg[:c[e]] >= 0).all() and (seg[c[e]:] == -1).all()
+        assert (np.diff(seg[:c[e]]) > 0).all()                # stable
+        assert (ids.ravel()[seg[:c[e]]] == e).all()
+    assert (s[off[E]:] == -1).all()
+    nb = off[E] // bm
+    assert (be[nb:] == -1).all()
+    for b in range(nb):
+        assert off[be[b]] <= b * bm < off[be[b] + 1]
+
+
+@pytest.mark.parametrize("T,E,k,bm,skew", [
+    (1, 8, 2, 16, None), (3, 8, 2, 32, None), (17, 128, 8, 16, None),
+    (64, 8, 2, 32, None), (200, 256, 8, 64, 1.2), (333, 16, 4, 128, 2.0),
+    (50, 1, 1, 16, None), (40, 6, 6, 16, None), (0, 8, 2, 32, None)])
+def test_align_invariants_and_bruteforce(T, E, k, bm, skew):
+    from workloads import make_topk_ids
+    ids = make_topk_ids(T, E, k, seed=5, skew=skew).numpy().reshape(T, k)
+    al = O.align(ids, E, bm)
+    _check_alignment_invariants(ids, E, bm, al)
+    # brute force: Python sort of (expert, flat index) pairs
+    pairs = sorted((int(e), i) for i, e in enumerate(ids.ravel()))
+    order = [i for _, i in pairs]
+    assert al["sorted_ids"][al["sorted_ids"] >= 0].tolist() == order
+
+
+def test_capacity_bound_is_attained():
+    # every active expert with a count of 1 mod bm attains the bound
+    bm, E = 8, 4
+    ids = np.array([[0], [1], [2], [3]])
+    al = O.align(ids, E, bm)
+    assert al["offsets"][E] == O.capacity(4, E, 1, bm) == 32
+
+
+# ---------------------------------------------------------------- experts
+
+def test_silu_identities():
+    z = np.linspace(-30, 30, 601)
+    s = O.silu(z)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert np.allclose(s - O.silu(-z), z, rtol=0, atol=1e-12)      # silu(z)-silu(-z)=z
+    assert np.allclose(s, torch.nn.functional.silu(torch.from_numpy(z)).numpy(), rtol=1e-14)
+    assert O.silu(np.array([-1000.0]))[0] == 0.0
+
+
+def _rand_layer(rng, E, d, dff):
+    wr = rng.standard_normal((d, E)) / math.sqrt(d)
+    wg = rng.standard_normal((E, d, dff)) / math.sqrt(d)
+    wu = rng.standard_normal((E, d, dff)) / math.sqrt(d)
+    wd = rng.standard_normal((E, dff, d)) / math.sqrt(dff)
+    return wr, wg, wu, wd
+
+
+def _fn(wg, wu, wd):
+    return lambda e: (wg[e], wu[e], wd[e])
+
+
+def test_single_expert_is_dense_swiglu_library():
+    # E = 1, k = 1: the layer reduces to a dense SwiGLU MLP; check it against
+    # torch's own matmul and silu in float64 (non-square shapes catch transposes)
+    rng = np.random.default_rng(1)
+    T, d, dff = 9, 12, 20
+    wr, wg, wu, wd = _rand_layer(rng, 1, d, dff)
+    x = rng.standard_normal((T, d))
+    res = O.moe_forward(x, wr, None, _fn(wg, wu, wd), 1, 1, 16)
+    tx = torch.from_numpy(x)
+    ref = (torch.nn.functional.silu(tx @ torch.from_numpy(wg[0])) * (tx @ torch.from_numpy(wu[0]))) \
+        @ torch.from_numpy(wd[0])
+    assert np.allclose(res["out"], ref.numpy(), rtol=1e-12, atol=1e-12)
+    assert (res["topk_w"] == 1.0).all()
+
+
+def test_identical_experts_make_output_router_independent():
+    rng = np.random.default_rng(2)
+    T, d, dff, E, k = 13, 10, 14, 6, 3
+    wr, wg, wu, wd = _rand_layer(rng, E, d, dff)
+    wg[:] = wg[0]
+    wu[:] = wu[0]
+    wd[:] = wd[0]
+    x = rng.standard_normal((T, d))
+    res = O.moe_forward(x, wr, rng.standard_normal(E), _fn(wg, wu, wd), E, k, 16)
+    dense = O.swiglu_expert(x, wg[0], wu[0], wd[0])
+    assert np.allclose(res["out"], dense, rtol=1e-12, atol=1e-12)
+
+
+def test_output_is_linear_in_down_weights_and_gate_up_order_matters():
+    rng = np.random.default_rng(4)
+    T, d, dff, E, k = 11, 8, 6, 4, 2
+    wr, wg, wu, wd = _rand_layer(rng, E, d, dff)
+    x = rng.standard_normal((T, d))
+    a = O.moe_forward(x, wr, None, _fn(wg, wu, wd), E, k, 16)["out"]
+    b = O.moe_forward(x, wr, None, _fn(wg, wu, 2.5 * wd), E, k, 16)["out"]
+    assert np.allclose(b, 2.5 * a, rtol=1e-12, atol=1e-13)
+    swapped = O.moe_forward(x, wr, None, _fn(wu, wg, wd), E, k, 16)["out"]
+    assert not np.allclose(swapped, a)
+
+
+def test_expert_weights_from_raw_layout_and_fp8_scales():
+    # gate columns first, then up; fp8 weight = decode(code) * scale[column]
+    E, d, dff = 2, 3, 2
+    codes = np.arange(E * d * 2 * dff, dtype=np.uint8).reshape(E, d, 2 * dff) + 56
+    dn = (np.arange(E * dff * d, dtype=np.uint8).reshape(E, dff, d) + 40)
+    sgu = np.arange(1, E * 2 * dff + 1, dtype=np.float32).reshape(E, 2 * dff)
+    sdn = np.full((E, d), 0.5, np.float32)
+    fn = O.expert_weights_from_raw(codes, dn, "fp8", sgu, sdn)
+    wg, wu, wd = fn(1)
+    full = O.decode_e4m3fn(codes[1]) * sgu[1][None, :]
+    assert (wg == full[:, :dff]).all() and (wu == full[:, dff:]).all()
+    assert (wd == O.decode_e4m3fn(dn[1]) * 0.5).all()
+    # factoring the column scale out of the dot product is exact in reals
+    a = np.array([0.25, -1.0, 2.0])
+    assert np.isclose(a @ wg[:, 1], sgu[1][1] * (a @ O.decode_e4m3fn(codes[1])[:, 1]))
+
+
+@pytest.mark.parametrize("T,E,k,d,dff,bias", [
+    (5, 4, 2, 6, 5, False), (7, 3, 3, 4, 3, True), (4, 8, 1, 5, 7, True)])
+def test_grouped_oracle_matches_bruteforce_loops(T, E, k, d, dff, bias):
+    rng = np.random.default_rng(T * 100 + E)
+    wr, wg, wu, wd = _rand_layer(rng, E, d, dff)
+    x = rng.standard_normal((T, d))
+    b = rng.standard_normal(E) if bias else None
+    res = O.moe_forward(x, wr, b, _fn(wg, wu, wd), E, k, 4, decision_dtype=None)
+    ids, w, out = O.moe_forward_bruteforce(x, wr, b, wg, wu, wd, k)
+    assert res["topk_ids"].tolist() == ids
+    assert np.allclose(res["topk_w"], w, rtol=1e-13, atol=1e-15)
+    assert np.allclose(res["out"], out, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.slow
+def test_tiny_fp32_layer_full_bruteforce():
+    """The 16-token fp32 layer (E=8, top-2, d=128, d_ff=256) in full against the
+    explicit loops."""
+    from workloads import CONFIGS, make_layer, make_tokens
+    sh = CONFIGS[0]
+    lay = make_layer(sh, 16)
+    x = O.decode_fp32(make_tokens(sh, 16).numpy())
+    wr = O.decode_fp32(lay.w_router.numpy())
+    gu = O.decode_fp32(lay.w_gate_up.numpy())
+    wd = O.decode_fp32(lay.w_down.numpy())
+    wg, wu = gu[:, :, :sh.d_ff], gu[:, :, sh.d_ff:]
+    res = O.moe_forward(x, wr, None, _fn(wg, wu, wd), sh.E, sh.k, 32, decision_dtype=None)
+    ids, w, out = O.moe_forward_bruteforce(x, wr, None, wg, wu, wd, sh.k)
+    assert res["topk_ids"].tolist() == ids
+    assert np.allclose(res["out"], out, rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------- accounting
+
+def test_gemm_accounting_matches_printed_4096_example():
+    from mixture_experts_layer_align_amd import roofline as R
+    g = json.load(open(os.path.join(GOLDEN, "gemm_4096_accounting.json")))
+    f = R.gemm_flops(g["M"], g["N"], g["K"])
+    assert f == 2 * 4096 ** 3
+    assert float(f"{f:.{g['printed_flops_sig_digits']}g}") == g["printed_flops"]
+    c = R.matrix_bytes(g["M"], g["N"], g["elem_bytes"])
+    # 33,554,432 B: the page prints it truncated to one decimal place of MB
+    assert math.floor(c / 1e5) / 10 == g["printed_C_megabytes"]
+    assert round(g["printed_epilogue_us"] / g["printed_gemm_us"], 2) == g["printed_epilogue_fraction"]

@@ -1,0 +1,153 @@
+"""Seeded generators of MoE layer inputs (weights, router bias, tokens).
+
+Every tensor is drawn from its own torch.Generator whose seed comes from
+numpy's SeedSequence([cfg_seed, tensor_id, index]); expert weights are drawn
+expert by expert so any single expert can be regenerated without the rest.
+
+Value laws (the workload statement's, with the readings documented alongside
+the oracle):
+  * x ~ N(0, 1), stored in the activation dtype (fp32, or bf16 by RNE).
+  * W_router[d, E], W_gate/W_up[E, d, d_ff] ~ N(0, 1/d); W_down[E, d_ff, d] ~
+    N(0, 1/d_ff)  (variance 1/fan_in), drawn in fp32 then stored in the weight
+    dtype.
+  * fp8 experts: per expert and per output column, scale = max_k |w[k, n]| / 448
+    (the OCP e4m3fn maximum), code = e4m3fn(w / scale) by torch's RNE cast; gate
+    and up columns are scaled separately.
+  * Zipf router skew: bias[e] = -s * ln(rank[e]) with rank a seeded permutation
+    of 1..E, which multiplies each expert's softmax mass by rank^-s.
+
+Generation may run on any torch device; values depend on that device's RNG, so
+a test feeds the oracle host copies of exactly the tensors the GPU consumed.
+"""
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from .configs import LayerShape
+
+FP8_MAX = 448.0
+
+TENSOR_X, TENSOR_WR, TENSOR_WG, TENSOR_WU, TENSOR_WD, TENSOR_PERM, TENSOR_IDS = range(7)
+
+_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _seed(*parts: int) -> int:
+    ss = np.random.SeedSequence([int(p) & 0xFFFFFFFF for p in parts])
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & 0x7FFFFFFFFFFFFFFF)
+
+
+def _gen(device, *parts: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed(*parts))
+    return g
+
+
+def _normal(shape, std, device, *parts):
+    g = _gen(device, *parts)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t
+
+
+def quantize_e4m3fn_per_column(w: torch.Tensor):
+    """w: [K, N] fp32 -> (codes [K, N] float8_e4m3fn, scale [N] fp32)."""
+    amax = w.abs().amax(dim=0)
+    scale = amax / FP8_MAX
+    scale = torch.where(amax > 0, scale, torch.ones_like(scale))
+    q = (w / scale).clamp_(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
+    return q, scale.to(torch.float32)
+
+
+@dataclass
+class Layer:
+    shape: LayerShape
+    w_router: torch.Tensor            # [d, E] act dtype
+    w_gate_up: torch.Tensor           # [E, d, 2*d_ff] weight dtype (gate cols first)
+    w_down: torch.Tensor              # [E, d_ff, d]
+    scale_gate_up: Optional[torch.Tensor]  # [E, 2*d_ff] fp32 (fp8 only)
+    scale_down: Optional[torch.Tensor]     # [E, d] fp32 (fp8 only)
+    bias: Optional[torch.Tensor]      # [E] fp32 router-logit bias or None
+
+    @property
+    def device(self):
+        return self.w_gate_up.device
+
+
+def make_bias(shape: LayerShape, s: Optional[float], device="cpu") -> Optional[torch.Tensor]:
+    if s is None:
+        return None
+    g = _gen("cpu", shape.seed, TENSOR_PERM, 0)
+    rank = torch.randperm(shape.E, generator=g).to(torch.float64) + 1.0
+    return (-float(s) * torch.log(rank)).to(torch.float32).to(device)
+
+
+def make_layer(shape: LayerShape, T: Optional[int] = None, device="cpu",
+               zipf: Optional[float] = "auto") -> Layer:
+    """Draw the layer of `shape` on `device`.
+
+    The router bias follows the shape's Zipf law for token count T unless
+    `zipf` is given explicitly (None for no bias)."""
+    E, d, dff = shape.E, shape.d, shape.d_ff
+    s = shape.seed
+    adt = _TORCH_DT[shape.act]
+    w_router = _normal((d, E), d ** -0.5, device, s, TENSOR_WR, 0).to(adt)
+    if shape.wdt == "fp8":
+        wgu = torch.empty((E, d, 2 * dff), dtype=torch.float8_e4m3fn, device=device)
+        wdn = torch.empty((E, dff, d), dtype=torch.float8_e4m3fn, device=device)
+        sgu = torch.empty((E, 2 * dff), dtype=torch.float32, device=device)
+        sdn = torch.empty((E, d), dtype=torch.float32, device=device)
+    else:
+        wdt = _TORCH_DT[shape.wdt]
+        wgu = torch.empty((E, d, 2 * dff), dtype=wdt, device=device)
+        wdn = torch.empty((E, dff, d), dtype=wdt, device=device)
+        sgu = sdn = None
+    for e in range(E):
+        wg = _normal((d, dff), d ** -0.5, device, s, TENSOR_WG, e)
+        wu = _normal((d, dff), d ** -0.5, device, s, TENSOR_WU, e)
+        wd = _normal((dff, d), dff ** -0.5, device, s, TENSOR_WD, e)
+        if shape.wdt == "fp8":
+            qg, sg = quantize_e4m3fn_per_column(wg)
+            qu, su = quantize_e4m3fn_per_column(wu)
+            qd, sd = quantize_e4m3fn_per_column(wd)
+            wgu[e, :, :dff] = qg
+            wgu[e, :, dff:] = qu
+            sgu[e, :dff] = sg
+            sgu[e, dff:] = su
+            wdn[e] = qd
+            sdn[e] = sd
+        else:
+            wgu[e, :, :dff] = wg.to(wgu.dtype)
+            wgu[e, :, dff:] = wu.to(wgu.dtype)
+            wdn[e] = wd.to(wdn.dtype)
+        del wg, wu, wd
+    if zipf == "auto":
+        zipf = shape.zipf_for(T) if T is not None else None
+    bias = make_bias(shape, zipf, device)
+    return Layer(shape, w_router, wgu, wdn, sgu, sdn, bias)
+
+
+def make_tokens(shape: LayerShape, T: int, device="cpu") -> torch.Tensor:
+    """x[T, d] ~ N(0, 1) in the activation dtype."""
+    x = _normal((T, shape.d), 1.0, device, shape.seed, TENSOR_X, T)
+    return x.to(_TORCH_DT[shape.act])
+
+
+def make_topk_ids(T: int, E: int, k: int, seed: int, skew: Optional[float] = None,
+                  device="cpu") -> torch.Tensor:
+    """Seeded routing tables for exercising alignment on its own: each row holds
+    k distinct expert ids.  With `skew`, experts are drawn with probability
+    proportional to rank^-skew (rank = 1 + expert id), otherwise uniformly."""
+    g = _gen("cpu", seed, TENSOR_IDS, T * 1315423911 + E * 2654435761 + k)
+    if skew is None:
+        keys = torch.rand((T, E), generator=g, dtype=torch.float64)
+    else:
+        w = torch.arange(1, E + 1, dtype=torch.float64).pow(-float(skew))
+        # Gumbel-top-k draws k distinct ids with the given sampling weights
+        u = torch.rand((T, E), generator=g, dtype=torch.float64).clamp_(1e-300, 1.0)
+        keys = torch.log(w)[None, :] - torch.log(-torch.log(u))
+    ids = torch.topk(keys, k, dim=1).indices.to(torch.int32)
+    return ids.to(device)
