@@ -1,0 +1,195 @@
+"""Benchmark of the fused MoE layer forward on one MI355X.
+
+A step is one moe_forward (router GEMM, top-k, alignment, gate|up GEMM with the
+SiLU*up epilogue, down GEMM, weighted combine) over one batch of synthetic
+tokens of the decode layer E=8, top-2, d=4096, d_ff=14336, bf16, with weights
+and tokens already resident in HBM.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--tokens T] [--config C]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="batch size (default: the largest decode batch of the config)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this layer is built and measured on a single "
+              "MI355X (no collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_align_amd import _binding as B
+    from mixture_experts_layer_align_amd import roofline as R
+    from workloads import CONFIGS, make_bias, make_layer, make_tokens
+
+    sh = CONFIGS[args.config]
+    decode_T = [t for t in sh.tokens if t <= 256]
+    T = args.tokens if args.tokens is not None else (max(decode_T) if decode_T else max(sh.tokens))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layer = make_layer(sh, None, dev, zipf=None)
+    bias = make_bias(sh, sh.zipf_for(T), dev)
+    fwd = B.Forward(layer.w_router, bias, layer.w_gate_up, layer.w_down, sh.k,
+                    layer.scale_gate_up, layer.scale_down)
+    stream = torch.cuda.current_stream()
+
+    def timed(x, steps, warmup):
+        out = torch.empty_like(x)
+        for _ in range(warmup):
+            fwd(x, out)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps):
+            fwd(x, out)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps, out
+
+    x = make_tokens(sh, T, dev)
+    torch.cuda.synchronize()
+    ms, out = timed(x, args.steps, args.warmup)
+
+    # per-kernel durations, HIP events recorded on the launch stream between
+    # the kernels of each forward
+    rb = fwd.routing_buffers(T)
+    _, bm, names = fwd(x, routing=rb)
+    torch.cuda.synchronize()
+    nk = len(names)
+    ev = B.HipEvents(nk + 1)
+    per = np.zeros(nk)
+    reps = max(args.steps, 10)
+    for _ in range(reps):
+        fwd(x, out, events=ev.handles)
+        torch.cuda.synchronize()
+        per += [ev.elapsed_ms(i, i + 1) for i in range(nk)]
+    per /= reps
+    kern = {n: float(v) for n, v in zip(names, per)}
+
+    counts = rb["counts"].cpu().numpy()
+    active = int((counts > 0).sum())
+    work = R.layer_work(T, sh.d, sh.d_ff, sh.E, sh.k, sh.act, sh.wdt, active)
+    dom = max(kern, key=kern.get)
+    dom_bytes = {"gate_up": work.bytes_gate_up, "down": work.bytes_down}.get(dom)
+    dom_flops = {"gate_up": work.flops_gate_up, "down": work.flops_down}.get(dom)
+    prefill = T * sh.k / sh.E > 256
+    if prefill:
+        achieved = dom_flops / (kern[dom] * 1e-3) / 1e12
+        peak = R.MFMA_BF16_FLOPS / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s"}
+    else:
+        achieved = dom_bytes / (kern[dom] * 1e-3) / 1e9
+        peak = R.HBM_BYTES_PER_S / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": peak, "unit": "GB/s"}
+    roof.update({"frac": achieved / peak, "traffic": None, "kernel": dom,
+                 "kernel_ms": kern[dom], "algorithmic_bytes_per_launch": dom_bytes,
+                 "algorithmic_flops_per_launch": dom_flops})
+
+    # other batch sizes of the same layer (same process, same weights)
+    sweep = {}
+    if not args.no_sweep:
+        for t2 in sh.tokens:
+            if t2 == T:
+                continue
+            f2 = B.Forward(layer.w_router, make_bias(sh, sh.zipf_for(t2), dev), layer.w_gate_up,
+                           layer.w_down, sh.k, layer.scale_gate_up, layer.scale_down)
+            fwd_saved = fwd
+            fwd = f2
+            x2 = make_tokens(sh, t2, dev)
+            m2, _ = timed(x2, max(args.steps // 2, 5), 3)
+            fwd = fwd_saved
+            sweep[str(t2)] = {"ms": m2, "tokens_per_s": t2 / (m2 * 1e-3)}
+
+    line = {
+        "metric": "MoE layer tokens/s; decode HBM GB/s, prefill MFMA TFLOP/s as % of peak",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if sh.wdt == "bf16" else ("f32" if sh.wdt == "f32" else "bf16-act/fp8-weight"),
+        "data": "synthetic",
+        "config": {"workload": f"fused MoE layer forward, {sh.name}: E={sh.E} top-{sh.k} "
+                               f"d={sh.d} d_ff={sh.d_ff} {sh.act} x / {sh.wdt} experts, T={T}",
+                   "tokens": T, "E": sh.E, "k": sh.k, "d": sh.d, "d_ff": sh.d_ff,
+                   "active_experts": active, "block_m": bm, "parallelism": "single GPU"},
+        "layer_hbm_GBps": work.bytes_total / (ms * 1e-3) / 1e9,
+        "layer_hbm_frac": work.bytes_total / (ms * 1e-3) / R.HBM_BYTES_PER_S,
+        "kernels_ms": kern,
+        "roofline": roof,
+        "sweep": sweep,
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(layer, bias, x, sh)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(layer, bias, x, sh):
+    """The oracle (float64 NumPy, as it stands) on the host cores, on the same
+    batch; tokens/s over its full forward including the decode of the stored
+    weights it reads."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import moe_oracle as O
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+
+    def bits(t):
+        t = t.detach()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        if t.dtype == torch.float8_e4m3fn:
+            return t.view(torch.uint8).cpu().numpy()
+        return t.cpu().numpy()
+
+    fmt = {"bf16": "bf16", "fp8": "fp8", "f32": "f32"}[sh.wdt]
+    gu = [bits(layer.w_gate_up[e]) for e in range(sh.E)]
+    dn = [bits(layer.w_down[e]) for e in range(sh.E)]
+    sgu = layer.scale_gate_up.cpu().numpy() if layer.scale_gate_up is not None else None
+    sdn = layer.scale_down.cpu().numpy() if layer.scale_down is not None else None
+    xb, wrb = bits(x), bits(layer.w_router)
+    b64 = None if bias is None else bias.cpu().numpy().astype(np.float64)
+    T = x.shape[0]
+    with threadpool_limits(limits=cores):
+        used = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        t0 = time.perf_counter()
+        efn = O.expert_weights_from_raw(gu, dn, fmt, sgu, sdn)
+        O.moe_forward(O.decode(xb, sh.act), O.decode(wrb, sh.act), b64, efn, sh.E, sh.k, 32)
+        dt = time.perf_counter() - t0
+    return {"value": T / dt, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"the full T={T} batch of the benchmarked layer (one oracle forward, "
+                      f"{dt:.1f} s, float64 NumPy incl. weight decode)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+/*
+ * libmoe — fused Mixture-of-Experts layer forward for AMD Instinct MI355X
+ * (gfx950).  C ABI.
+ *
+ * The layer, per token t with hidden vector x[t] (length d):
+ *   1. router logits   L[t, e] = sum_i x[t, i] * W_r[i, e] + bias[e]
+ *   2. routing         ids[t, 0..k-1] = the k largest logits, slot j holding the
+ *                      j-th largest (ties to the lower expert index), and
+ *                      w[t, j] = softmax(L[t])[ids[t, j]] renormalised over the
+ *                      k selected experts (so the k weights sum to 1);
+ *   3. alignment       a per-expert count of the routed (t, j) entries and a
+ *                      unique slot for each entry inside its expert's padded
+ *                      range of the expert-sorted row buffer;
+ *   4. gate|up GEMM    h[p] = SiLU(x[t] W_gate[e]) * (x[t] W_up[e]) for every
+ *                      slot p holding entry (t, j) of expert e;
+ *   5. down GEMM       y[p] = h[p] W_down[e];
+ *   6. combine         out[t] = sum_j w[t, j] * y[slot of (t, j)].
+ *
+ * Sources: "CuTeDSL at Perplexity", section on MoE dispatch and combine, local
+ * (TP=1) kernel (routing table, per-expert counts, a unique index per token in
+ * its expert's list, optionally padded per-expert buffers, a combine that
+ * accumulates weighted expert outputs from those positions); the vLLM fused-MoE
+ * post, section "Swap-AB" (expert compute A[M,K] x B[K,N] -> C[M,N], so expert
+ * weights are stored [K, N]); "La fusion de noyaux", section 4.2 (SwiGLU and the
+ * concatenated d x 2*d_ff gate|up GEMM with the activation applied in the GEMM
+ * epilogue).  The router rule (softmax, top-k with ties to the lower index,
+ * renormalisation) is the workload statement's; the pages leave it open.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise; arrays are dense,
+ *     row-major, and 16-byte aligned.  `stream` is a hipStream_t (NULL: the
+ *     default stream).  All work is enqueued on `stream`; the library never
+ *     synchronises, never allocates or frees device memory and never prints.
+ *     Outputs are valid once the stream reaches that point.
+ *   - The caller owns every buffer.  Weights are read-only and must outlive the
+ *     enqueued work.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is enqueued.  A launch failure reported by the runtime
+ *     returns MOE_ERR_DEVICE; faults inside kernels surface at the caller's
+ *     next synchronisation.
+ *   - T == 0 is valid and enqueues nothing.
+ *   - Workspace: entry points that need scratch take (workspace,
+ *     workspace_bytes).  With workspace == NULL the call only writes the
+ *     required size to *workspace_bytes and returns MOE_OK.  Otherwise
+ *     *workspace_bytes must be at least that size (MOE_ERR_WORKSPACE if not)
+ *     and the workspace must be 256-byte aligned.  Its contents on entry do not
+ *     matter.  Calls that overlap in time must not share a workspace.
+ *   - Results are deterministic: integer outputs never depend on scheduling
+ *     (no atomics decide an order), and floating-point sums run in a fixed
+ *     order, so a repeated call gives bitwise-identical outputs.
+ */
+#ifndef LIBMOE_H
+#define LIBMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = -1,      /* NULL required pointer, bad size or range      */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but not built: dtype mix, shape modulus */
+  MOE_ERR_WORKSPACE = -3,    /* workspace smaller than required, or misaligned */
+  MOE_ERR_DEVICE = -4        /* the HIP runtime refused a launch or query     */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,        /* IEEE binary32                                       */
+  MOE_BF16 = 1,       /* bfloat16                                            */
+  MOE_FP8_E4M3 = 2    /* OCP FP8 E4M3 ("e4m3fn": max 448, no infinities)     */
+} moe_dtype;
+
+/* Supported dtype combinations (activation / router weight, expert weight):
+ * (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).  FP8 expert weights carry one
+ * fp32 scale per expert and output column; the GEMM multiplies its fp32
+ * accumulator by that scale in the epilogue (W = code * scale).             */
+
+/* Allowed alignment block sizes (rows of one padded block). */
+#define MOE_BLOCK_M_MIN 16
+#define MOE_BLOCK_M_MAX 256
+#define MOE_MAX_EXPERTS 1024
+
+/* Rows of the padded, expert-sorted buffer for T tokens, E experts, top-k and
+ * block size bm: each active expert pads its count to a multiple of bm and at
+ * most min(E, T*k) experts are active, so
+ *   capacity = bm * floor((T*k + min(E, T*k) * (bm - 1)) / bm).
+ * Host function; returns -1 for invalid arguments.                           */
+int64_t moe_align_capacity(int T, int E, int k, int block_m);
+
+/* ---------------------------------------------------------------------------
+ * moe_route — steps 1 and 2 (router logits, softmax, top-k, renormalisation).
+ * "CuTeDSL at Perplexity", MoE dispatch and combine: the router's routing
+ * table that dispatch consumes; rule from the workload statement.
+ *
+ *   x          [T, d]  act_dtype (MOE_F32 or MOE_BF16)
+ *   w_router   [d, E]  act_dtype
+ *   logit_bias [E]     fp32, added to every token's logits before selection
+ *                      and softmax; NULL for none
+ *   logits     [T, E]  fp32 out (bias included), or NULL
+ *   topk_ids   [T, k]  int32 out; slot j = j-th largest logit, ties -> lower id
+ *   topk_w     [T, k]  fp32 out; softmax over E restricted to the selected
+ *                      experts and renormalised to sum 1
+ * Logits accumulate in fp32; the top-k decision is taken on those fp32 values.
+ * Limits: 1 <= k <= E <= MOE_MAX_EXPERTS, d % 64 == 0, T >= 0.
+ * ------------------------------------------------------------------------- */
+int moe_route(const void* x, const void* w_router, const float* logit_bias,
+              int T, int d, int E, int k, int act_dtype,
+              float* logits, int32_t* topk_ids, float* topk_w,
+              void* workspace, size_t* workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_align — step 3 (histogram -> padded exclusive scan -> stable scatter).
+ * "CuTeDSL at Perplexity", MoE dispatch and combine, local kernel: count the
+ * tokens routed to each expert, give each a unique index in its expert's list,
+ * lay the lists out in optionally padded per-expert buffers.
+ *
+ *   topk_ids       [T, k] int32 in, every id in [0, E), distinct within a row
+ *   expert_counts  [E]    int32 out: entries routed to each expert
+ *   padded_offsets [E+1]  int32 out: 0, then running sum of counts rounded up
+ *                         to a multiple of block_m
+ *   sorted_ids     [cap]  int32 out, cap = moe_align_capacity(T, E, k, block_m):
+ *                         sorted_ids[padded_offsets[e] + r] = t*k + j for the
+ *                         r-th entry (in ascending t*k + j) routed to e; every
+ *                         other slot = -1
+ *   inv_pos        [T*k]  int32 out: the slot of entry t*k + j
+ *   block_expert   [cap/block_m] int32 out: expert owning each block_m-row
+ *                         block, -1 for blocks at or past padded_offsets[E]
+ * block_m must be a power of two in [MOE_BLOCK_M_MIN, MOE_BLOCK_M_MAX].
+ * No atomics decide the order: the result is unique and reproducible.
+ * Out-of-range ids are a caller error (not checked on the device).
+ * ------------------------------------------------------------------------- */
+int moe_align(const int32_t* topk_ids, int T, int E, int k, int block_m,
+              int32_t* expert_counts, int32_t* padded_offsets,
+              int32_t* sorted_ids, int32_t* inv_pos, int32_t* block_expert,
+              void* workspace, size_t* workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_forward — the whole layer, steps 1-6.
+ * Expert GEMMs follow the A[M,K] x B[K,N] statement of the vLLM fused-MoE post
+ * (section "Swap-AB"): B = expert weight [K, N], N contiguous.  Gate and up are
+ * concatenated into one [d, 2*d_ff] matrix, gate columns first ("La fusion de
+ * noyaux", section 4.2); SiLU(g)*u is applied to the fp32 accumulators before
+ * the single store of h.  The top-k weights are applied in the combine.
+ * Intermediates h and y are stored in the activation dtype.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int d, d_ff, E, k;
+  int act_dtype;                /* MOE_F32 or MOE_BF16: x, out, w_router      */
+  int w_dtype;                  /* MOE_F32, MOE_BF16 or MOE_FP8_E4M3         */
+  const void* w_router;         /* [d, E] act_dtype                           */
+  const float* logit_bias;      /* [E] fp32 or NULL                           */
+  const void* w_gate_up;        /* [E, d, 2*d_ff]; cols [0,d_ff) gate,
+                                   [d_ff, 2*d_ff) up                          */
+  const void* w_down;           /* [E, d_ff, d]                               */
+  const float* scale_gate_up;   /* [E, 2*d_ff] fp32, FP8 weights only        */
+  const float* scale_down;      /* [E, d] fp32, FP8 weights only             */
+} moe_layer;
+
+/* Optional copies of the routing the forward computed.  Any pointer may be
+ * NULL.  Sizes as for moe_route / moe_align with block_m = the value the
+ * forward chose, which it writes to *block_m (host pointer) when non-NULL;
+ * sorted_ids must hold moe_align_capacity(T, E, k, MOE_BLOCK_M_MAX) entries
+ * so it fits whatever block size the forward picks.                          */
+typedef struct {
+  float* logits;             /* [T, E]   */
+  int32_t* topk_ids;         /* [T, k]   */
+  float* topk_w;             /* [T, k]   */
+  int32_t* expert_counts;    /* [E]      */
+  int32_t* padded_offsets;   /* [E+1]    */
+  int32_t* sorted_ids;       /* [cap]    */
+  int32_t* inv_pos;          /* [T*k]    */
+  int* block_m;              /* host out */
+} moe_routing_out;
+
+/* Optional per-kernel timing: when non-NULL, `events` holds n_events
+ * hipEvent_t handles (created by the caller) and the forward records
+ * events[i] on `stream` before its i-th kernel and events[n] after the last;
+ * n_kernels receives the number of kernels enqueued.  Used only for
+ * measurement; recording adds no work to the kernels themselves.            */
+typedef struct {
+  void** events;
+  int n_events;
+  int n_kernels;             /* out */
+  const char* names[16];     /* out: kernel names, in launch order */
+} moe_trace;
+
+/*   x    [T, d] act_dtype;  out [T, d] act_dtype (may not alias x).
+ * Limits: 1 <= k <= E <= MOE_MAX_EXPERTS, d % 128 == 0, d_ff % 128 == 0,
+ * T * k < 2^31, a supported dtype pair, FP8 scales present for FP8 weights. */
+int moe_forward(const moe_layer* layer, const void* x, int T, void* out,
+                void* workspace, size_t* workspace_bytes,
+                moe_routing_out* routing, void* stream);
+
+int moe_forward_traced(const moe_layer* layer, const void* x, int T, void* out,
+                       void* workspace, size_t* workspace_bytes,
+                       moe_routing_out* routing, moe_trace* trace, void* stream);
+
+/* Static description of a status code (host). */
+const char* moe_status_string(int status);
+
+/* ABI version, bumped on any incompatible change. */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMOE_H */

@@ -1,0 +1,374 @@
+// C ABI of libmoe: argument validation, workspace layout, launch order.
+// The ABI itself is documented in include/libmoe.h.
+#include <algorithm>
+#include <cstring>
+
+#include "../../include/libmoe.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int64_t WS_ALIGN = 256;
+constexpr int TARGET_WAVES = 2048;   // waves worth launching at once (8 per CU)
+constexpr int64_t MAX_ENTRIES = int64_t(1) << 24;
+
+int64_t up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Bump allocator over the caller's workspace (or a size count when base==NULL).
+struct Carve {
+  char* base;
+  int64_t off = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(int64_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off = up(off + count * (int64_t)sizeof(T), WS_ALIGN);
+    return p;
+  }
+};
+
+int act_code(int dt) { return dt == MOE_BF16 ? ACT_BF16 : ACT_F32; }
+int w_code(int dt) { return dt == MOE_FP8_E4M3 ? W_FP8 : (dt == MOE_BF16 ? W_BF16 : W_F32); }
+int act_bytes(int dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int check_ws(void* ws, size_t* ws_bytes, int64_t need, bool* query) {
+  if (ws_bytes == nullptr) return MOE_ERR_INVALID;
+  if (ws == nullptr) {
+    *ws_bytes = (size_t)need;
+    *query = true;
+    return MOE_OK;
+  }
+  *query = false;
+  if ((int64_t)*ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % WS_ALIGN != 0) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+// Split K so that items * split waves approach TARGET_WAVES, keeping at least
+// two k-steps per split.  Returns the k-chunk (a multiple of kstep).
+int choose_kchunk(int64_t items, int K, int kstep, int* nsplit) {
+  const int steps = K / kstep;
+  items = std::max<int64_t>(items, 1);
+  int s = 1;
+  if (items < TARGET_WAVES) s = (int)std::min<int64_t>((TARGET_WAVES + items - 1) / items, steps / 2);
+  s = std::max(s, 1);
+  const int chunk_steps = (steps + s - 1) / s;
+  *nsplit = (steps + chunk_steps - 1) / chunk_steps;
+  return chunk_steps * kstep;
+}
+
+// ------------------------------------------------------------ router plan
+struct RouterPlan {
+  StreamGemmArgs g;
+  int nsplit;
+  int64_t partial_floats;
+};
+
+RouterPlan plan_router(const void* x, const void* w_router, int T, int d, int E, int act) {
+  RouterPlan r{};
+  const int wdt = (act == ACT_BF16) ? W_BF16 : W_F32;
+  StreamGemmArgs& g = r.g;
+  g.a = x;
+  g.a_ld = d;
+  g.a_mode = A_DENSE;
+  g.m_total = T;
+  g.block_expert = nullptr;
+  g.num_mblocks = (T + STREAM_BM - 1) / STREAM_BM;
+  g.w = w_router;
+  g.w_ld = E;
+  g.w_estride = 0;
+  g.K = d;
+  g.n_out = E;
+  const int tc = stream_tile_cols(wdt, EPI_F32);
+  g.n_tiles = (E + tc - 1) / tc;
+  g.kchunk = choose_kchunk((int64_t)g.num_mblocks * g.n_tiles, d, stream_kstep(wdt), &g.ksplit);
+  g.out_ld = E;
+  g.out_split_stride = (int64_t)T * E;
+  r.nsplit = g.ksplit;
+  r.partial_floats = (int64_t)g.ksplit * T * E;
+  return r;
+}
+
+hipError_t run_router(RouterPlan& r, int act, float* partial, const float* bias, int T, int E,
+                      int k, float* logits, int32_t* ids, float* w, int32_t* zero_ptr,
+                      int64_t zero_n, hipStream_t st, moe_trace* tr, int* kidx);
+
+// ------------------------------------------------------------ tracing
+void trace_mark(moe_trace* tr, int* kidx, const char* name, hipStream_t st) {
+  if (tr == nullptr) return;
+  if (*kidx < tr->n_events && tr->events != nullptr)
+    (void)hipEventRecord(reinterpret_cast<hipEvent_t>(tr->events[*kidx]), st);
+  if (name != nullptr && *kidx < 16) tr->names[*kidx] = name;
+  ++*kidx;
+}
+
+hipError_t run_router(RouterPlan& r, int act, float* partial, const float* bias, int T, int E,
+                      int k, float* logits, int32_t* ids, float* w, int32_t* zero_ptr,
+                      int64_t zero_n, hipStream_t st, moe_trace* tr, int* kidx) {
+  r.g.out = partial;
+  trace_mark(tr, kidx, "router_gemm", st);
+  hipError_t e = launch_stream_gemm(act, act == ACT_BF16 ? W_BF16 : W_F32, EPI_F32, r.g, st);
+  if (e != hipSuccess) return e;
+  trace_mark(tr, kidx, "topk", st);
+  return launch_topk(partial, r.nsplit, (int64_t)T * E, bias, T, E, k, logits, ids, w, zero_ptr,
+                     zero_n, st);
+}
+
+int validate_route(const void* x, const void* w_router, int T, int d, int E, int k, int act) {
+  if (T < 0 || d <= 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID;
+  if (k > E || E > MOE_MAX_EXPERTS) return MOE_ERR_INVALID;
+  if ((int64_t)T * k >= MAX_ENTRIES) return MOE_ERR_INVALID;
+  if (act != MOE_F32 && act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (x == nullptr || w_router == nullptr)) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return 1; }
+
+const char* moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_DEVICE: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int64_t moe_align_capacity(int T, int E, int k, int bm) {
+  if (T < 0 || E <= 0 || k <= 0 || !pow2(bm)) return -1;
+  const int64_t n = (int64_t)T * k;
+  if (n == 0) return 0;
+  return (int64_t)bm * ((n + std::min<int64_t>(E, n) * (bm - 1)) / bm);
+}
+
+int moe_route(const void* x, const void* w_router, const float* logit_bias, int T, int d, int E,
+              int k, int act_dtype, float* logits, int32_t* topk_ids, float* topk_w,
+              void* workspace, size_t* workspace_bytes, void* stream) {
+  int rc = validate_route(x, w_router, T, d, E, k, act_dtype);
+  if (rc != MOE_OK) return rc;
+  if (T > 0 && (topk_ids == nullptr || topk_w == nullptr)) return MOE_ERR_INVALID;
+  const int act = act_code(act_dtype);
+  RouterPlan r = plan_router(x, w_router, T, d, E, act);
+  Carve c(workspace);
+  float* partial = c.take<float>(std::max<int64_t>(r.partial_floats, 1));
+  bool query;
+  rc = check_ws(workspace, workspace_bytes, c.off, &query);
+  if (rc != MOE_OK || query || T == 0) return rc;
+  int kidx = 0;
+  hipError_t e = run_router(r, act, partial, logit_bias, T, E, k, logits, topk_ids, topk_w,
+                            nullptr, 0, static_cast<hipStream_t>(stream), nullptr, &kidx);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+int moe_align(const int32_t* topk_ids, int T, int E, int k, int block_m, int32_t* expert_counts,
+              int32_t* padded_offsets, int32_t* sorted_ids, int32_t* inv_pos,
+              int32_t* block_expert, void* workspace, size_t* workspace_bytes, void* stream) {
+  if (T < 0 || E <= 0 || k <= 0 || k > E || E > MOE_MAX_EXPERTS) return MOE_ERR_INVALID;
+  if (!pow2(block_m) || block_m < MOE_BLOCK_M_MIN || block_m > MOE_BLOCK_M_MAX)
+    return MOE_ERR_INVALID;
+  const int64_t n = (int64_t)T * k;
+  if (n >= MAX_ENTRIES) return MOE_ERR_INVALID;
+  if (T > 0 && (topk_ids == nullptr || expert_counts == nullptr || padded_offsets == nullptr ||
+                sorted_ids == nullptr || inv_pos == nullptr || block_expert == nullptr))
+    return MOE_ERR_INVALID;
+  const int64_t need = align_workspace_bytes((int)n, E);
+  bool query;
+  int rc = check_ws(workspace, workspace_bytes, need, &query);
+  if (rc != MOE_OK || query) return rc;
+  if (T == 0) return MOE_OK;
+  AlignArgs a{};
+  a.ids = topk_ids;
+  a.n = (int)n;
+  a.T = T;
+  a.E = E;
+  a.k = k;
+  a.bm = block_m;
+  a.cap = moe_align_capacity(T, E, k, block_m);
+  a.counts = expert_counts;
+  a.offsets = padded_offsets;
+  a.sorted_ids = sorted_ids;
+  a.inv_pos = inv_pos;
+  a.block_expert = block_expert;
+  hipError_t e = launch_align(a, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void* workspace,
+                       size_t* workspace_bytes, moe_routing_out* routing, moe_trace* tr,
+                       void* stream) {
+  if (L == nullptr) return MOE_ERR_INVALID;
+  const int d = L->d, dff = L->d_ff, E = L->E, k = L->k;
+  int rc = validate_route(x, L->w_router, T, d, E, k, L->act_dtype);
+  if (rc != MOE_OK) return rc;
+  if (dff <= 0) return MOE_ERR_INVALID;
+  if (d % 128 != 0 || dff % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  const bool pair_ok = (L->act_dtype == MOE_F32 && L->w_dtype == MOE_F32) ||
+                       (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_BF16) ||
+                       (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_FP8_E4M3);
+  if (!pair_ok) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (L->w_gate_up == nullptr || L->w_down == nullptr || out == nullptr))
+    return MOE_ERR_INVALID;
+  if (L->w_dtype == MOE_FP8_E4M3 && (L->scale_gate_up == nullptr || L->scale_down == nullptr))
+    return MOE_ERR_INVALID;
+  if (T > 0 && out == x) return MOE_ERR_INVALID;
+
+  const int act = act_code(L->act_dtype);
+  const int wdt = w_code(L->w_dtype);
+  const int ab = act_bytes(L->act_dtype);
+  const int bm = STREAM_BM;
+  const int64_t n = (int64_t)T * k;
+  const int64_t cap = moe_align_capacity(T, E, k, bm);
+  const int64_t nblocks = cap / bm;
+
+  RouterPlan r = plan_router(x, L->w_router, T, d, E, act);
+
+  // expert GEMM plans
+  const int kstep = stream_kstep(wdt);
+  const int gu_tc = stream_tile_cols(wdt, EPI_SILU_MUL);
+  const int dn_tc = stream_tile_cols(wdt, EPI_STORE);
+  const int gu_tiles = dff / gu_tc;
+  const int dn_tiles = (d + dn_tc - 1) / dn_tc;
+  // blocks expected to carry rows: one per active expert plus the overflow
+  const int64_t est_blocks =
+      std::min<int64_t>(nblocks, std::max<int64_t>(std::min<int64_t>(E, n), (n + bm - 1) / bm));
+  int gu_split, dn_split;
+  const int gu_chunk = choose_kchunk(std::max<int64_t>(est_blocks, 1) * gu_tiles, d, kstep, &gu_split);
+  const int dn_chunk = choose_kchunk(std::max<int64_t>(est_blocks, 1) * dn_tiles, dff, kstep, &dn_split);
+  const int64_t pf = stream_partial_floats_per_tile_split(wdt);
+  const int64_t gu_partial = gu_split > 1 ? nblocks * gu_tiles * gu_split * pf : 0;
+  const int64_t dn_partial = dn_split > 1 ? nblocks * dn_tiles * dn_split * pf : 0;
+  const int64_t ncounters = nblocks * std::max(gu_tiles, dn_tiles);
+
+  Carve c(workspace);
+  float* r_partial = c.take<float>(std::max<int64_t>(r.partial_floats, 1));
+  int32_t* ids = c.take<int32_t>(std::max<int64_t>(n, 1));
+  float* tw = c.take<float>(std::max<int64_t>(n, 1));
+  int32_t* counts = c.take<int32_t>(E);
+  int32_t* offs = c.take<int32_t>(E + 1);
+  int32_t* sorted = c.take<int32_t>(std::max<int64_t>(cap, 1));
+  int32_t* inv = c.take<int32_t>(std::max<int64_t>(n, 1));
+  int32_t* bexp = c.take<int32_t>(std::max<int64_t>(nblocks, 1));
+  char* al_ws = c.take<char>(std::max<int64_t>(align_workspace_bytes((int)n, E), 1));
+  char* h = c.take<char>(std::max<int64_t>(cap * dff * ab, 1));
+  char* y = c.take<char>(std::max<int64_t>(cap * d * ab, 1));
+  float* gpart = c.take<float>(std::max<int64_t>(std::max(gu_partial, dn_partial), 1));
+  int32_t* counters = c.take<int32_t>(std::max<int64_t>(ncounters, 1));
+  bool query;
+  rc = check_ws(workspace, workspace_bytes, c.off, &query);
+  if (rc != MOE_OK || query) return rc;
+  if (routing != nullptr && routing->block_m != nullptr) *routing->block_m = bm;
+  if (tr != nullptr) tr->n_kernels = 0;
+  if (T == 0) return MOE_OK;
+
+  // routing views the caller asked for are written in place
+  if (routing != nullptr) {
+    if (routing->topk_ids) ids = routing->topk_ids;
+    if (routing->topk_w) tw = routing->topk_w;
+    if (routing->expert_counts) counts = routing->expert_counts;
+    if (routing->padded_offsets) offs = routing->padded_offsets;
+    if (routing->sorted_ids) sorted = routing->sorted_ids;
+    if (routing->inv_pos) inv = routing->inv_pos;
+  }
+  float* logits = routing ? routing->logits : nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int kidx = 0;
+
+  hipError_t e = run_router(r, act, r_partial, L->logit_bias, T, E, k, logits, ids, tw, counters,
+                            ncounters, st, tr, &kidx);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+
+  AlignArgs a{};
+  a.ids = ids;
+  a.n = (int)n;
+  a.T = T;
+  a.E = E;
+  a.k = k;
+  a.bm = bm;
+  a.cap = cap;
+  a.counts = counts;
+  a.offsets = offs;
+  a.sorted_ids = sorted;
+  a.inv_pos = inv;
+  a.block_expert = bexp;
+  trace_mark(tr, &kidx, "align", st);
+  e = launch_align(a, al_ws, st);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+
+  StreamGemmArgs g{};
+  g.a = x;
+  g.a_ld = d;
+  g.a_mode = A_GATHER;
+  g.sorted_ids = sorted;
+  g.topk = k;
+  g.block_expert = bexp;
+  g.num_mblocks = (int)nblocks;
+  g.w = L->w_gate_up;
+  g.w_ld = 2 * (int64_t)dff;
+  g.w_estride = (int64_t)d * 2 * dff;
+  g.scale = L->scale_gate_up;
+  g.scale_estride = 2 * (int64_t)dff;
+  g.K = d;
+  g.n_out = dff;
+  g.up_off = dff;
+  g.n_tiles = gu_tiles;
+  g.ksplit = gu_split;
+  g.kchunk = gu_chunk;
+  g.partial = gpart;
+  g.counters = counters;
+  g.out = h;
+  g.out_ld = dff;
+  trace_mark(tr, &kidx, "gate_up", st);
+  e = launch_stream_gemm(act, wdt, EPI_SILU_MUL, g, st);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+
+  StreamGemmArgs g2{};
+  g2.a = h;
+  g2.a_ld = dff;
+  g2.a_mode = A_PADDED;
+  g2.sorted_ids = sorted;
+  g2.topk = k;
+  g2.block_expert = bexp;
+  g2.num_mblocks = (int)nblocks;
+  g2.w = L->w_down;
+  g2.w_ld = d;
+  g2.w_estride = (int64_t)dff * d;
+  g2.scale = L->scale_down;
+  g2.scale_estride = d;
+  g2.K = dff;
+  g2.n_out = d;
+  g2.n_tiles = dn_tiles;
+  g2.ksplit = dn_split;
+  g2.kchunk = dn_chunk;
+  g2.partial = gpart;
+  g2.counters = counters;
+  g2.out = y;
+  g2.out_ld = d;
+  trace_mark(tr, &kidx, "down", st);
+  e = launch_stream_gemm(act, wdt, EPI_STORE, g2, st);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+
+  trace_mark(tr, &kidx, "combine", st);
+  e = launch_combine(act, y, inv, tw, T, k, d, out, st);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  trace_mark(tr, &kidx, nullptr, st);
+  if (tr != nullptr) tr->n_kernels = kidx - 1;
+  return MOE_OK;
+}
+
+int moe_forward(const moe_layer* L, const void* x, int T, void* out, void* workspace,
+                size_t* workspace_bytes, moe_routing_out* routing, void* stream) {
+  return moe_forward_traced(L, x, T, out, workspace, workspace_bytes, routing, nullptr, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Host-side launch interface between the C ABI (moe_api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int MAX_EXPERTS = 1024;
+
+enum { ACT_F32 = 0, ACT_BF16 = 1 };             // activation storage
+enum { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };      // expert-weight storage
+
+// ------------------------------------------------------------ stream GEMM
+//
+// Weight-streaming grouped GEMM: one wave per work item (m-block of 32 rows,
+// n-tile, k-split).  Every wave streams its [k-range, n-tile] panel of one
+// expert's weight once, straight from HBM into registers, and multiplies it
+// with all rows of its block.
+
+enum { A_DENSE = 0,    // row p = input row p, valid when p < m_total
+       A_GATHER = 1,   // row p = input row sorted_ids[p] / topk, valid when >= 0
+       A_PADDED = 2 }; // row p = input row p, valid when sorted_ids[p] >= 0
+
+enum { EPI_SILU_MUL = 0,  // two slabs (gate, up) -> act dtype  h = silu(g)*u
+       EPI_STORE = 1,     // two adjacent slabs -> act dtype
+       EPI_F32 = 2 };     // two adjacent slabs -> fp32, no reduction; split s
+                          // writes its own [m_total, ld] plane
+
+struct StreamGemmArgs {
+  const void* a;          // row source
+  int64_t a_ld;           // elements
+  int a_mode;
+  const int32_t* sorted_ids;
+  int topk;
+  int m_total;            // A_DENSE: valid row count
+  const int32_t* block_expert;  // NULL: dense, expert 0
+  int num_mblocks;
+  const void* w;          // weights [E][K][w_ld]
+  int64_t w_ld;
+  int64_t w_estride;
+  const float* scale;     // fp8: [E][scale_ld] per weight column, else NULL
+  int64_t scale_estride;
+  int K;
+  int n_out;              // output columns
+  int up_off;             // EPI_SILU_MUL: column of the first "up" weight column
+  int n_tiles;
+  int ksplit;
+  int kchunk;
+  float* partial;         // split-K partial tiles (ksplit > 1)
+  int32_t* counters;      // one per (m-block, n-tile), zero on entry
+  void* out;
+  int64_t out_ld;
+  int64_t out_split_stride;  // EPI_F32: elements between split planes
+};
+
+// Rows per m-block of the stream GEMM (two 16-row MFMA column groups).
+constexpr int STREAM_BM = 32;
+
+// Output columns covered by one n-tile of the stream GEMM.
+int stream_tile_cols(int w_dtype, int epi);
+// K granularity of one k-step.
+int stream_kstep(int w_dtype);
+// Floats of partial storage one (tile, split) needs.
+int64_t stream_partial_floats_per_tile_split(int w_dtype);
+
+hipError_t launch_stream_gemm(int act_dtype, int w_dtype, int epi, const StreamGemmArgs& a,
+                              hipStream_t st);
+
+// ------------------------------------------------------------ routing
+
+// Sum split-K partial logits, add bias, write logits (optional), select top-k
+// with ties to the lower index and renormalised softmax weights.  Also zeroes
+// `zero_ptr[0..zero_n)` (counters used by later kernels of the same call).
+hipError_t launch_topk(const float* partial, int nsplit, int64_t split_stride, const float* bias,
+                       int T, int E, int k, float* logits, int32_t* ids, float* w,
+                       int32_t* zero_ptr, int64_t zero_n, hipStream_t st);
+
+// ------------------------------------------------------------ alignment
+
+struct AlignArgs {
+  const int32_t* ids;
+  int n;             // T * k entries
+  int T, E, k, bm;
+  int64_t cap;       // padded capacity (rows)
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_ids;
+  int32_t* inv_pos;
+  int32_t* block_expert;
+  // multi-tile scratch
+  int32_t* tile_hist;   // [ntiles][E]
+  int32_t* rank;        // [n]
+  int ntiles;
+};
+
+constexpr int ALIGN_SINGLE_MAX = 4096;   // entries one workgroup aligns alone
+constexpr int ALIGN_TILE = 4096;         // entries per tile of the multi-pass path
+
+int64_t align_workspace_bytes(int n, int E);
+hipError_t launch_align(AlignArgs a, void* ws, hipStream_t st);
+
+// ------------------------------------------------------------ combine
+
+hipError_t launch_combine(int act_dtype, const void* y, const int32_t* inv_pos, const float* w,
+                          int T, int k, int d, void* out, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,377 @@
+// Routing (softmax / top-k / renormalisation) and expert alignment.
+//
+// Routing: one wave per token.  Each lane holds E/64 logits; k rounds of a
+// wave-wide butterfly argmax pick the slots in descending order with ties to
+// the lower index, and the renormalised softmax weight of slot j is
+// exp(L_j - L_max) / sum_j' exp(L_j' - L_max) (the softmax denominator over all
+// E cancels in the renormalisation).  The butterfly shuffles are the gfx950
+// form of the sub-warp horizontal reductions of "CuTeDSL at Perplexity"
+// (section on QK-norm, and the half-/quarter-warp reductions of its Blackwell
+// section).
+//
+// Alignment ("CuTeDSL at Perplexity", MoE dispatch and combine, local kernel:
+// count the tokens of each expert and give every token a unique index in its
+// expert's list; prefill spreads the routing over many blocks with a global
+// aggregation).  The pages assign slots with shared-memory atomic counters,
+// which makes the order within an expert depend on scheduling.  Here every
+// step is integer and order-preserving, so the permutation is the unique
+// stable one:
+//   * per 64-entry chunk, lanes holding the same expert find each other with
+//     log2(E) ballots (a "match" mask); the lane's rank among equal lanes below
+//     it is a popcount; the lowest such lane adds the chunk count to its
+//     wave's running per-expert histogram in LDS (one writer per address);
+//   * per expert, an exclusive prefix over waves (and, for large inputs, over
+//     4096-entry tiles) turns local ranks into ranks within the expert;
+//   * an exclusive scan of counts rounded up to the block size gives the padded
+//     offsets; entry i lands at offsets[e] + rank.
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// ================================================================ top-k
+
+__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+
+template <int V>
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial, int nsplit,
+                                              int64_t split_stride, const float* __restrict__ bias,
+                                              int T, int E, int k, float* __restrict__ logits,
+                                              int32_t* __restrict__ ids, float* __restrict__ wout,
+                                              int32_t* __restrict__ zero_ptr, int64_t zero_n) {
+  __shared__ float sel_v[4][MAX_EXPERTS];
+  __shared__ int sel_i[4][MAX_EXPERTS];
+  for (int64_t z = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; z < zero_n;
+       z += (int64_t)gridDim.x * blockDim.x)
+    zero_ptr[z] = 0;
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+
+  float v[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int e = lane + 64 * j;
+    float s = -INFINITY;
+    if (e < E) {
+      const float* pp = partial + (int64_t)t * E + e;
+      s = pp[0];
+      for (int sp = 1; sp < nsplit; ++sp) s += pp[sp * split_stride];
+      if (bias != nullptr) s += bias[e];
+      if (logits != nullptr) logits[(int64_t)t * E + e] = s;
+    }
+    v[j] = s;
+  }
+
+  for (int r = 0; r < k; ++r) {
+    float bv = v[0];
+    int bi = lane;
+#pragma unroll
+    for (int j = 1; j < V; ++j)
+      if (better(v[j], lane + 64 * j, bv, bi)) {
+        bv = v[j];
+        bi = lane + 64 * j;
+      }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        if (bi == lane + 64 * j) v[j] = -INFINITY;
+    }
+    if (lane == 0) {
+      sel_v[wave][r] = bv;
+      sel_i[wave][r] = bi;
+    }
+  }
+  // weights: exp(L_j - L_0) / sum, the sum as a fixed butterfly
+  const float l0 = sel_v[wave][0];
+  float part = 0.f;
+  for (int r = lane; r < k; r += 64) part += expf(sel_v[wave][r] - l0);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+  const float inv = 1.0f / part;
+  for (int r = lane; r < k; r += 64) {
+    ids[(int64_t)t * k + r] = sel_i[wave][r];
+    wout[(int64_t)t * k + r] = expf(sel_v[wave][r] - l0) * inv;
+  }
+}
+
+hipError_t launch_topk(const float* partial, int nsplit, int64_t split_stride, const float* bias,
+                       int T, int E, int k, float* logits, int32_t* ids, float* w,
+                       int32_t* zero_ptr, int64_t zero_n, hipStream_t st) {
+  const int grid = (T + 3) / 4;
+  if (grid == 0) return hipSuccess;
+#define MOE_TOPK(V_)                                                                           \
+  hipLaunchKernelGGL(k_topk<V_>, dim3(grid), dim3(256), 0, st, partial, nsplit, split_stride, \
+                     bias, T, E, k, logits, ids, w, zero_ptr, zero_n)
+  if (E <= 64) MOE_TOPK(1);
+  else if (E <= 128) MOE_TOPK(2);
+  else if (E <= 256) MOE_TOPK(4);
+  else if (E <= 512) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
+  return hipGetLastError();
+}
+
+// ================================================================ alignment
+
+constexpr int AL_THREADS = 1024;
+constexpr int AL_WAVES = AL_THREADS / 64;
+constexpr int AL_CHUNKS_PER_WAVE = ALIGN_TILE / (AL_WAVES * 64);  // 4
+
+static_assert(ALIGN_SINGLE_MAX == ALIGN_TILE, "single-workgroup path covers one tile");
+
+// Block-wide exclusive scan of one int per thread (1024 threads).  Returns the
+// exclusive prefix; *total receives the sum.  Fixed order, integer exact.
+__device__ int block_exscan(int x, int* sh /* [AL_WAVES + 1] */, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) sh[wave] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < AL_WAVES; ++w) {
+      const int c = sh[w];
+      sh[w] = run;
+      run += c;
+    }
+    sh[AL_WAVES] = run;
+  }
+  __syncthreads();
+  const int ex = sh[wave] + inc - x;
+  *total = sh[AL_WAVES];
+  __syncthreads();
+  return ex;
+}
+
+// Processes the entries [i0, i0 + cnt) of one tile with 16 waves: fills
+// hist[w][e] with each wave's per-expert count and returns, per lane and chunk,
+// the entry's expert and its rank among the same-expert entries of its wave
+// that precede it.  After return (and a barrier) hist holds per-wave counts.
+struct ChunkState {
+  int e[AL_CHUNKS_PER_WAVE];
+  int r[AL_CHUNKS_PER_WAVE];
+};
+
+__device__ ChunkState tile_local_ranks(const int32_t* __restrict__ ids, int64_t i0, int cnt, int E,
+                                       int nbits, int* hist /* [AL_WAVES][E] */) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int x = threadIdx.x; x < AL_WAVES * E; x += AL_THREADS) hist[x] = 0;
+  __syncthreads();
+  ChunkState cs;
+  int* h = hist + wave * E;
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int c = 0; c < AL_CHUNKS_PER_WAVE; ++c) {
+    const int local = (wave * AL_CHUNKS_PER_WAVE + c) * 64 + lane;
+    const bool valid = local < cnt;
+    const int e = valid ? ids[i0 + local] : 0;
+    uint64_t mask = ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = ballot(valid && bit);
+      mask &= bit ? m : ~m;
+    }
+    const int below = __popcll(mask & lt);
+    int r = 0;
+    if (valid) r = h[e] + below;
+    // all reads of this chunk precede the leader's update (in-order LDS per wave)
+    __builtin_amdgcn_wave_barrier();
+    if (valid && below == 0) h[e] += __popcll(mask);
+    __builtin_amdgcn_wave_barrier();
+    cs.e[c] = valid ? e : -1;
+    cs.r[c] = r;
+  }
+  __syncthreads();
+  return cs;
+}
+
+// Turns hist[w][e] (per-wave counts) into exclusive per-wave prefixes and
+// returns the tile total of expert e = threadIdx.x (threads >= E return 0).
+__device__ int hist_wave_prefix(int* hist, int E) {
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int w = 0; w < AL_WAVES; ++w) {
+      const int c = hist[w * E + e];
+      hist[w * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  return run;
+}
+
+// counts/offsets known (in LDS): write counts, offsets, padding -1 slots and
+// block_expert.  Called by one workgroup.
+__device__ void write_layout(const AlignArgs& a, const int* s_counts, const int* s_off) {
+  const int E = a.E, bm = a.bm;
+  for (int e = threadIdx.x; e < E; e += AL_THREADS) {
+    a.counts[e] = s_counts[e];
+    a.offsets[e] = s_off[e];
+    for (int s = s_off[e] + s_counts[e]; s < s_off[e + 1]; ++s) a.sorted_ids[s] = -1;
+    for (int b = s_off[e] / bm; b < s_off[e + 1] / bm; ++b) a.block_expert[b] = e;
+  }
+  if (threadIdx.x == 0) a.offsets[E] = s_off[E];
+  for (int64_t s = s_off[E] + threadIdx.x; s < a.cap; s += AL_THREADS) a.sorted_ids[s] = -1;
+  for (int64_t b = s_off[E] / bm + threadIdx.x; b < a.cap / bm; b += AL_THREADS)
+    a.block_expert[b] = -1;
+}
+
+__device__ __forceinline__ int ilog2_ceil(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+// One workgroup aligns all entries (n <= ALIGN_TILE).
+__global__ __launch_bounds__(AL_THREADS) void k_align_single(const AlignArgs a) {
+  extern __shared__ int lds[];
+  int* hist = lds;                          // [AL_WAVES][E]
+  int* s_counts = hist + AL_WAVES * a.E;    // [E]
+  int* s_off = s_counts + a.E;              // [E + 1]
+  int* sh = s_off + a.E + 1;                // [AL_WAVES + 1]
+  const int E = a.E;
+  const ChunkState cs = tile_local_ranks(a.ids, 0, a.n, E, ilog2_ceil(E), hist);
+  const int cnt = hist_wave_prefix(hist, E);
+  int padded = 0;
+  if ((int)threadIdx.x < E) padded = (cnt + a.bm - 1) / a.bm * a.bm;
+  int total;
+  const int ex = block_exscan(padded, sh, &total);
+  if ((int)threadIdx.x < E) {
+    s_counts[threadIdx.x] = cnt;
+    s_off[threadIdx.x] = ex;
+  }
+  if (threadIdx.x == 0) s_off[E] = total;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int c = 0; c < AL_CHUNKS_PER_WAVE; ++c) {
+    const int e = cs.e[c];
+    if (e < 0) continue;
+    const int i = (wave * AL_CHUNKS_PER_WAVE + c) * 64 + lane;
+    const int pos = s_off[e] + hist[wave * E + e] + cs.r[c];
+    a.sorted_ids[pos] = i;
+    a.inv_pos[i] = pos;
+  }
+  write_layout(a, s_counts, s_off);
+}
+
+// Multi-tile pass 1: per-tile histogram and rank of each entry in its tile.
+__global__ __launch_bounds__(AL_THREADS) void k_align_hist(const AlignArgs a) {
+  extern __shared__ int lds[];
+  int* hist = lds;
+  const int E = a.E;
+  const int64_t i0 = (int64_t)blockIdx.x * ALIGN_TILE;
+  const int cnt = (int)min<int64_t>(ALIGN_TILE, a.n - i0);
+  const ChunkState cs = tile_local_ranks(a.ids, i0, cnt, E, ilog2_ceil(E), hist);
+  const int tot = hist_wave_prefix(hist, E);
+  if ((int)threadIdx.x < E) a.tile_hist[(int64_t)blockIdx.x * E + threadIdx.x] = tot;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int c = 0; c < AL_CHUNKS_PER_WAVE; ++c) {
+    const int e = cs.e[c];
+    if (e < 0) continue;
+    const int local = (wave * AL_CHUNKS_PER_WAVE + c) * 64 + lane;
+    a.rank[i0 + local] = hist[wave * E + e] + cs.r[c];
+  }
+}
+
+// Multi-tile pass 2: global counts and padded offsets (each workgroup redoes
+// the small scan), then the scatter of this tile's entries; workgroup 0 also
+// writes the layout arrays.
+__global__ __launch_bounds__(AL_THREADS) void k_align_scatter(const AlignArgs a) {
+  extern __shared__ int lds[];
+  const int E = a.E;
+  int* s_counts = lds;            // [E]
+  int* s_off = s_counts + E;      // [E + 1]
+  int* s_tbase = s_off + E + 1;   // [E]
+  int* sh = s_tbase + E;          // [AL_WAVES + 1]
+  const int e = threadIdx.x;
+  int cnt = 0, before = 0;
+  if (e < E) {
+    for (int t = 0; t < a.ntiles; ++t) {
+      const int c = a.tile_hist[(int64_t)t * E + e];
+      if (t < (int)blockIdx.x) before += c;
+      cnt += c;
+    }
+  }
+  const int padded = (e < E) ? (cnt + a.bm - 1) / a.bm * a.bm : 0;
+  int total;
+  const int ex = block_exscan(padded, sh, &total);
+  if (e < E) {
+    s_counts[e] = cnt;
+    s_off[e] = ex;
+    s_tbase[e] = ex + before;
+  }
+  if (threadIdx.x == 0) s_off[E] = total;
+  __syncthreads();
+  const int64_t i0 = (int64_t)blockIdx.x * ALIGN_TILE;
+  const int cntt = (int)min<int64_t>(ALIGN_TILE, a.n - i0);
+  for (int l = threadIdx.x; l < cntt; l += AL_THREADS) {
+    const int64_t i = i0 + l;
+    const int ee = a.ids[i];
+    const int pos = s_tbase[ee] + a.rank[i];
+    a.sorted_ids[pos] = (int)i;
+    a.inv_pos[i] = pos;
+  }
+  if (blockIdx.x == 0) write_layout(a, s_counts, s_off);
+}
+
+int64_t align_workspace_bytes(int n, int E) {
+  if (n <= ALIGN_SINGLE_MAX) return 0;
+  const int64_t ntiles = (n + ALIGN_TILE - 1) / ALIGN_TILE;
+  const int64_t hist = ntiles * E * 4;
+  return ((hist + 255) / 256) * 256 + (int64_t)n * 4;
+}
+
+hipError_t launch_align(AlignArgs a, void* ws, hipStream_t st) {
+  if (a.n == 0) {
+    return hipSuccess;
+  }
+  if (a.n <= ALIGN_SINGLE_MAX) {
+    const size_t lds = ((size_t)AL_WAVES * a.E + 2 * a.E + 1 + AL_WAVES + 1) * 4;
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute((const void*)k_align_single,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_align_single, dim3(1), dim3(AL_THREADS), lds, st, a);
+    return hipGetLastError();
+  }
+  a.ntiles = (a.n + ALIGN_TILE - 1) / ALIGN_TILE;
+  const int64_t hist = (int64_t)a.ntiles * a.E * 4;
+  a.tile_hist = reinterpret_cast<int32_t*>(ws);
+  a.rank = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + ((hist + 255) / 256) * 256);
+  const size_t lds1 = (size_t)AL_WAVES * a.E * 4;
+  if (lds1 > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_align_hist,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_align_hist, dim3(a.ntiles), dim3(AL_THREADS), lds1, st, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t lds2 = ((size_t)3 * a.E + 1 + AL_WAVES + 1) * 4;
+  hipLaunchKernelGGL(k_align_scatter, dim3(a.ntiles), dim3(AL_THREADS), lds2, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

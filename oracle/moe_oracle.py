@@ -59,12 +59,12 @@ def decode_fp32(a: np.ndarray) -> np.ndarray:
     return np.asarray(a, dtype=np.float32).astype(np.float64)
 
 
-def decode_e4m3fn(bits: np.ndarray) -> np.ndarray:
+def _e4m3fn_value(b: np.ndarray) -> np.ndarray:
     """OCP 8-bit float E4M3 ("fn": finite, no infinities): 1 sign bit, 4 exponent
     bits with bias 7, 3 mantissa bits; exponent field 0 encodes subnormals
     m/8 * 2^-6; the all-ones pattern S.1111.111 is NaN; the largest finite
     magnitude is 1.75 * 2^8 = 448."""
-    b = np.asarray(bits).astype(np.uint8).astype(np.int64)
+    b = np.asarray(b).astype(np.int64)
     sign = np.where(b & 0x80, -1.0, 1.0)
     e = (b >> 3) & 0xF
     m = (b & 0x7).astype(np.float64)
@@ -72,6 +72,13 @@ def decode_e4m3fn(bits: np.ndarray) -> np.ndarray:
     subnormal = (m / 8.0) * 2.0 ** -6
     v = sign * np.where(e == 0, subnormal, normal)
     return np.where((e == 15) & ((b & 0x7) == 7), np.nan, v)
+
+
+def decode_e4m3fn(bits: np.ndarray) -> np.ndarray:
+    """Decode OCP e4m3fn codes: the value of each of the 256 codes from the
+    format definition above, looked up per element."""
+    table = _e4m3fn_value(np.arange(256))
+    return table[np.asarray(bits).astype(np.uint8)]
 
 
 def decode(raw: np.ndarray, fmt: str) -> np.ndarray:
@@ -242,14 +249,25 @@ def moe_forward(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray],
     return res
 
 
-def token_forward(x_t: np.ndarray, ids_t, w_t, expert_fn: ExpertFn) -> np.ndarray:
-    """out for one token given its routing (for sampled checks of big layers)."""
-    x_t = np.asarray(x_t, np.float64)[None, :]
-    acc = np.zeros(x_t.shape[1])
-    for e, wj in zip(ids_t, w_t):
-        wg, wu, wd = expert_fn(int(e))
-        acc += float(wj) * swiglu_expert(x_t, wg, wu, wd)[0]
-    return acc
+def outputs_for_tokens(x: np.ndarray, rows, ids: np.ndarray, w: np.ndarray,
+                       expert_fn: ExpertFn) -> np.ndarray:
+    """O6-O7 for the token rows `rows` only, given the routing (ids, w) of all
+    tokens: out[t] = sum_j w[t, j] * SwiGLU_{ids[t, j]}(x[t]).  Each needed expert
+    is fetched once (sampled checks of layers too large to run in full)."""
+    x = np.asarray(x, np.float64)
+    rows = np.asarray(rows, np.int64)
+    out = np.zeros((rows.size, x.shape[1]))
+    need: Dict[int, list] = {}
+    for r, t in enumerate(rows):
+        for j, e in enumerate(np.asarray(ids)[t]):
+            need.setdefault(int(e), []).append((r, int(t), j))
+    for e in sorted(need):
+        wg, wu, wd = expert_fn(e)
+        items = need[e]
+        Y = swiglu_expert(x[[t for _, t, _ in items]], wg, wu, wd)
+        for (r, t, j), yrow in zip(items, Y):
+            out[r] += w[t, j] * yrow
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -1,0 +1,128 @@
+"""The C-ABI library loads and exports every entry point include/libmoe.h
+declares; host-side logic (capacity, validation, workspace queries) behaves as
+documented.  Nothing here launches a kernel: every call either fails
+validation or is a workspace query, both of which return before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from mixture_experts_layer_align_amd import _binding as B
+from oracle import moe_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "libmoe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    declared = _declared()
+    assert set(declared) >= {"moe_route", "moe_align", "moe_forward"}
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(declared) == sorted(B.EXPORTED)
+
+
+def test_abi_version_and_status_strings():
+    lib = B.load()
+    assert lib.moe_abi_version() == 1
+    for s in (B.MOE_OK, B.MOE_ERR_INVALID, B.MOE_ERR_UNSUPPORTED, B.MOE_ERR_WORKSPACE,
+              B.MOE_ERR_DEVICE):
+        assert len(B.status_string(s)) > 0
+
+
+@pytest.mark.parametrize("T,E,k,bm", [(0, 8, 2, 32), (1, 8, 2, 32), (5, 4, 2, 4), (64, 8, 2, 32),
+                                      (256, 128, 8, 16), (16384, 256, 8, 128), (3, 1024, 7, 256)])
+def test_capacity_matches_oracle(T, E, k, bm):
+    assert B.align_capacity(T, E, k, bm) == O.capacity(T, E, k, bm)
+
+
+def test_capacity_rejects_bad_block():
+    assert B.align_capacity(4, 8, 2, 24) == -1
+    assert B.align_capacity(-1, 8, 2, 32) == -1
+
+
+def _route(T=4, d=128, E=8, k=2, act=B.MOE_BF16, x=1, w=1, ids=1, tw=1, ws=None):
+    lib = B.load()
+    n = ctypes.c_size_t(0)
+    vp = ctypes.c_void_p
+    return lib.moe_route(vp(x) if x else None, vp(w) if w else None, None, T, d, E, k, act, None,
+                         vp(ids) if ids else None, vp(tw) if tw else None, ws, ctypes.byref(n),
+                         None), n.value
+
+
+def test_route_validation_errors_before_any_launch():
+    assert _route(k=9, E=8)[0] == B.MOE_ERR_INVALID
+    assert _route(k=0)[0] == B.MOE_ERR_INVALID
+    assert _route(E=2000, k=2)[0] == B.MOE_ERR_INVALID
+    assert _route(T=-1)[0] == B.MOE_ERR_INVALID
+    assert _route(d=100)[0] == B.MOE_ERR_UNSUPPORTED
+    assert _route(act=B.MOE_FP8_E4M3)[0] == B.MOE_ERR_UNSUPPORTED
+    assert _route(x=0)[0] == B.MOE_ERR_INVALID
+    rc, need = _route()
+    assert rc == B.MOE_OK and need > 0          # workspace query
+    assert _route(T=0, x=0, w=0, ids=0, tw=0)[0] == B.MOE_OK
+
+
+def test_align_validation_errors():
+    lib = B.load()
+    n = ctypes.c_size_t(0)
+    vp = ctypes.c_void_p
+    p = vp(1)
+    args = lambda T, E, k, bm: (p, T, E, k, bm, p, p, p, p, p, None, ctypes.byref(n), None)
+    assert lib.moe_align(*args(4, 8, 2, 24)) == B.MOE_ERR_INVALID   # not a power of two
+    assert lib.moe_align(*args(4, 8, 2, 8)) == B.MOE_ERR_INVALID    # below 16
+    assert lib.moe_align(*args(4, 8, 2, 512)) == B.MOE_ERR_INVALID  # above 256
+    assert lib.moe_align(*args(4, 2, 3, 32)) == B.MOE_ERR_INVALID   # k > E
+    assert lib.moe_align(*args(4, 8, 2, 32)) == B.MOE_OK            # query
+    assert n.value == 0                                             # one workgroup, no scratch
+    assert lib.moe_align(*args(3000, 8, 2, 32)) == B.MOE_OK
+    assert n.value > 0                                              # multi-tile scratch
+    assert lib.moe_align(None, 4, 8, 2, 32, p, p, p, p, p, None, ctypes.byref(n), None) \
+        == B.MOE_ERR_INVALID
+
+
+def _layer(**kw):
+    L = B.MoeLayer()
+    L.d, L.d_ff, L.E, L.k = kw.get("d", 256), kw.get("d_ff", 256), kw.get("E", 8), kw.get("k", 2)
+    L.act_dtype, L.w_dtype = kw.get("act", B.MOE_BF16), kw.get("wdt", B.MOE_BF16)
+    L.w_router, L.w_gate_up, L.w_down = 1, 1, 1
+    L.scale_gate_up = kw.get("sgu", None)
+    L.scale_down = kw.get("sdn", None)
+    return L
+
+
+def _fwd(L, T=4, ws=None, nbytes=0, x=8, out=16):
+    lib = B.load()
+    n = ctypes.c_size_t(nbytes)
+    vp = ctypes.c_void_p
+    rc = lib.moe_forward(ctypes.byref(L), vp(x) if x else None, T, vp(out) if out else None,
+                         ws, ctypes.byref(n), None, None)
+    return rc, n.value
+
+
+def test_forward_validation_and_workspace_query():
+    assert _fwd(_layer())[0] == B.MOE_OK
+    assert _fwd(_layer(d=192))[0] == B.MOE_ERR_UNSUPPORTED
+    assert _fwd(_layer(d_ff=200))[0] == B.MOE_ERR_UNSUPPORTED
+    assert _fwd(_layer(act=B.MOE_F32, wdt=B.MOE_BF16))[0] == B.MOE_ERR_UNSUPPORTED
+    assert _fwd(_layer(act=B.MOE_F32, wdt=B.MOE_FP8_E4M3, sgu=1, sdn=1))[0] == B.MOE_ERR_UNSUPPORTED
+    assert _fwd(_layer(wdt=B.MOE_FP8_E4M3))[0] == B.MOE_ERR_INVALID     # scales missing
+    assert _fwd(_layer(wdt=B.MOE_FP8_E4M3, sgu=1, sdn=1))[0] == B.MOE_OK
+    assert _fwd(_layer(k=9))[0] == B.MOE_ERR_INVALID
+    assert _fwd(_layer(), x=8, out=8)[0] == B.MOE_ERR_INVALID           # out aliases x
+    # a given workspace smaller than the requirement is refused before any launch
+    _, need = _fwd(_layer(), T=64)
+    assert need > 0
+    assert _fwd(_layer(), T=64, ws=ctypes.c_void_p(4096), nbytes=need - 1)[0] == B.MOE_ERR_WORKSPACE
+    assert _fwd(_layer(), T=64, ws=ctypes.c_void_p(4096 + 8), nbytes=need)[0] == B.MOE_ERR_WORKSPACE
+    # workspace grows with T
+    assert _fwd(_layer(), T=4096)[1] > need

@@ -1,0 +1,133 @@
+"""moe_forward (the whole layer) against the oracle.
+
+Small layers run the oracle in full; the five benchmark layers run at their
+full sizes in the launch configuration the benchmark uses, with every integer
+output checked in full and the float output checked on all tokens (decode) or
+on a seeded sample of tokens (prefill)."""
+import dataclasses
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import parity as P
+from mixture_experts_layer_align_amd import _binding as B
+from oracle import moe_oracle as O
+from workloads import CONFIGS, LayerShape, make_bias, make_layer, make_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+def run_and_check(layer, x, sample=None, what=""):
+    sh = layer.shape
+    T = x.shape[0]
+    fwd = B.Forward(layer.w_router, layer.bias, layer.w_gate_up, layer.w_down, sh.k,
+                    layer.scale_gate_up, layer.scale_down)
+    rb = fwd.routing_buffers(T)
+    out, bm, _ = fwd(x, routing=rb)
+    torch.cuda.synchronize()
+    if T == 0:
+        return out, rb, bm
+    wr64, b64, efn = P.oracle_layer(layer)
+    x64 = P.decode(x)
+    L64, oids, ow = O.route(x64, wr64, b64, sh.k)
+    # routing
+    P.assert_close_f32(rb["logits"].cpu().numpy(), L64, f"{what} logits")
+    gids = rb["topk_ids"].cpu().numpy()
+    ties = P.classify_ids(L64, gids, oids)
+    assert ties.size <= max(1, T // 100), f"{what}: {ties.size} near ties"
+    keep = np.setdiff1d(np.arange(T), ties)
+    P.assert_close_f32(rb["topk_w"].cpu().numpy()[keep], ow[keep], f"{what} topk_w")
+    # alignment
+    cap = O.capacity(T, sh.E, sh.k, bm)
+    got = {k_: rb[k_].cpu().numpy() for k_ in ("counts", "offsets", "sorted_ids", "inv_pos")}
+    got["sorted_ids"] = got["sorted_ids"][:cap]
+    got["inv_pos"] = got["inv_pos"][:T * sh.k]
+    if ties.size == 0:
+        ref = O.align(oids, sh.E, bm)
+        for key in got:
+            assert (got[key] == ref[key]).all(), f"{what}: {key}"
+    else:
+        P.check_alignment_properties(gids, sh.E, bm, got["counts"], got["offsets"],
+                                     got["sorted_ids"], got["inv_pos"])
+    # output
+    rows = keep if sample is None else np.setdiff1d(sample, ties)
+    ref_out = O.outputs_for_tokens(x64, rows, oids, ow, efn)
+    o = P.decode(out)[rows]
+    P.assert_out_close(o, ref_out, sh.act, what)
+    return out, rb, bm
+
+
+SMALL = [
+    # E, k, d, d_ff, act, wdt, T, zipf
+    (8, 2, 128, 256, "f32", "f32", 16, None),
+    (8, 2, 128, 128, "bf16", "bf16", 1, None),
+    (8, 2, 256, 384, "bf16", "bf16", 33, None),
+    (16, 4, 384, 256, "bf16", "bf16", 100, 1.0),     # d a multiple of 128, not of 256
+    (1, 1, 128, 128, "bf16", "bf16", 70, None),      # a single expert: dense SwiGLU
+    (6, 6, 256, 128, "bf16", "bf16", 9, None),       # k = E: every token on every expert
+    (32, 8, 512, 256, "bf16", "fp8", 40, 1.2),
+    (128, 8, 256, 128, "bf16", "bf16", 3, None),     # most experts empty
+    (8, 2, 256, 256, "bf16", "fp8", 257, 1.2),
+    (4, 2, 128, 128, "f32", "f32", 300, 0.5),
+    (8, 2, 128, 128, "bf16", "bf16", 0, None),       # empty batch
+]
+
+
+@pytest.mark.parametrize("E,k,d,d_ff,act,wdt,T,zipf", SMALL)
+def test_forward_small_layers(E, k, d, d_ff, act, wdt, T, zipf):
+    sh = LayerShape(200 + E, "small", E=E, k=k, d=d, d_ff=d_ff, act=act, wdt=wdt,
+                    seed=500 + E * 3 + d + T)
+    print(f"forward small E={E} k={k} d={d} d_ff={d_ff} {act}/{wdt} T={T}", flush=True)
+    layer = make_layer(sh, T, "cuda", zipf=zipf)
+    x = make_tokens(sh, T, "cuda")
+    run_and_check(layer, x, what="small")
+
+
+def test_forward_all_tokens_on_one_expert_in_full_blocks():
+    # a one-hot bias sends every token's slot 0 to expert 3; 64 tokens fill
+    # exactly two 32-row blocks
+    sh = LayerShape(250, "onehot", E=8, k=1, d=256, d_ff=128, act="bf16", wdt="bf16", seed=9)
+    layer = make_layer(sh, 64, "cuda", zipf=None)
+    bias = torch.zeros(8, dtype=torch.float32, device="cuda")
+    bias[3] = 1e4
+    layer = dataclasses.replace(layer, bias=bias)
+    x = make_tokens(sh, 64, "cuda")
+    _, rb, bm = run_and_check(layer, x, what="one-hot")
+    c = rb["counts"].cpu().numpy()
+    assert c[3] == 64 and c.sum() == 64 and 64 % bm == 0
+
+
+def test_forward_is_deterministic():
+    sh = CONFIGS[3]
+    layer = make_layer(sh, 256, "cuda")
+    x = make_tokens(sh, 256, "cuda")
+    fwd = B.Forward(layer.w_router, layer.bias, layer.w_gate_up, layer.w_down, sh.k)
+    a = fwd(x)[0].clone()
+    b = fwd(x)[0].clone()
+    assert torch.equal(a, b)
+
+
+@functools.lru_cache(maxsize=1)
+def _config_layer(cfg):
+    torch.cuda.empty_cache()
+    return make_layer(CONFIGS[cfg], None, "cuda", zipf=None)
+
+
+FULL = [(c, T) for c in sorted(CONFIGS) for T in CONFIGS[c].tokens]
+
+
+@pytest.mark.parametrize("cfg,T", FULL)
+def test_forward_benchmark_layers_full_size(cfg, T):
+    sh = CONFIGS[cfg]
+    print(f"forward config {cfg} ({sh.name}) T={T}", flush=True)
+    base = _config_layer(cfg)
+    layer = dataclasses.replace(base, bias=make_bias(sh, sh.zipf_for(T), "cuda"))
+    x = make_tokens(sh, T, "cuda")
+    sample = None
+    if T > (64 if cfg == 4 else 256):
+        # the float output on a seeded sample (every integer output in full)
+        rng = np.random.default_rng(cfg * 100003 + T)
+        sample = np.sort(rng.choice(T, size=24 if cfg == 4 else 48, replace=False))
+    run_and_check(layer, x, sample=sample, what=f"config {cfg} T={T}")

@@ -322,3 +322,14 @@ def test_gemm_accounting_matches_printed_4096_example():
     # 33,554,432 B: the page prints it truncated to one decimal place of MB
     assert math.floor(c / 1e5) / 10 == g["printed_C_megabytes"]
     assert round(g["printed_epilogue_us"] / g["printed_gemm_us"], 2) == g["printed_epilogue_fraction"]
+
+
+def test_outputs_for_tokens_matches_grouped_forward():
+    rng = np.random.default_rng(8)
+    T, d, dff, E, k = 12, 6, 5, 5, 2
+    wr, wg, wu, wd = _rand_layer(rng, E, d, dff)
+    x = rng.standard_normal((T, d))
+    res = O.moe_forward(x, wr, None, _fn(wg, wu, wd), E, k, 16)
+    rows = [11, 0, 5]
+    sub = O.outputs_for_tokens(x, rows, res["topk_ids"], res["topk_w"], _fn(wg, wu, wd))
+    assert np.allclose(sub, res["out"][rows], rtol=1e-13, atol=1e-14)

@@ -7,4 +7,4 @@ tests and the GPU path can take their inputs from here without sharing any
 computation.
 """
 from .configs import CONFIGS, LayerShape, layer_shape  # noqa: F401
-from .gen import make_layer, make_tokens, make_topk_ids, Layer  # noqa: F401
+from .gen import Layer, make_bias, make_layer, make_router, make_tokens, make_topk_ids  # noqa: F401

@@ -85,6 +85,13 @@ def make_bias(shape: LayerShape, s: Optional[float], device="cpu") -> Optional[t
     return (-float(s) * torch.log(rank)).to(torch.float32).to(device)
 
 
+def make_router(shape: LayerShape, device="cpu") -> torch.Tensor:
+    """W_router[d, E] ~ N(0, 1/d) in the activation dtype (the same draw
+    make_layer uses)."""
+    return _normal((shape.d, shape.E), shape.d ** -0.5, device, shape.seed, TENSOR_WR, 0).to(
+        _TORCH_DT[shape.act])
+
+
 def make_layer(shape: LayerShape, T: Optional[int] = None, device="cpu",
                zipf: Optional[float] = "auto") -> Layer:
     """Draw the layer of `shape` on `device`.
@@ -93,8 +100,7 @@ def make_layer(shape: LayerShape, T: Optional[int] = None, device="cpu",
     `zipf` is given explicitly (None for no bias)."""
     E, d, dff = shape.E, shape.d, shape.d_ff
     s = shape.seed
-    adt = _TORCH_DT[shape.act]
-    w_router = _normal((d, E), d ** -0.5, device, s, TENSOR_WR, 0).to(adt)
+    w_router = make_router(shape, device)
     if shape.wdt == "fp8":
         wgu = torch.empty((E, d, 2 * dff), dtype=torch.float8_e4m3fn, device=device)
         wdn = torch.empty((E, dff, d), dtype=torch.float8_e4m3fn, device=device)
