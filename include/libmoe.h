@@ -144,7 +144,7 @@ int moe_align(const int32_t* topk_ids, int T, int E, int k, int block_m,
  * concatenated into one [d, 2*d_ff] matrix, gate columns first ("La fusion de
  * noyaux", section 4.2); SiLU(g)*u is applied to the fp32 accumulators before
  * the single store of h.  The top-k weights are applied in the combine.
- * Intermediates h and y are stored in the activation dtype.
+ * Intermediates: h in the activation dtype, the per-slot expert outputs y in fp32.
  * ------------------------------------------------------------------------- */
 typedef struct {
   int d, d_ff, E, k;

@@ -3,21 +3,21 @@
 // "CuTeDSL at Perplexity", MoE dispatch and combine, local kernel: combine
 // accumulates each token's expert outputs in registers, vectorised, using the
 // routing weights and the positions dispatch assigned.  Here a workgroup
-// handles one token: each thread owns 8 (bf16) or 4 (fp32) consecutive
-// elements, loads the k expert rows with 16-byte loads and sums them in fp32
-// in slot order j = 0..k-1, then rounds once to the activation dtype.
+// handles one token: each thread owns 8 (bf16 output) or 4 (fp32 output)
+// consecutive elements, loads the k fp32 expert rows with 16-byte loads and
+// sums them in fp32 in slot order j = 0..k-1, then rounds once to the
+// activation dtype.
 #include "moe_common.h"
 #include "moe_internal.h"
 
 namespace moe {
 
 template <int ACT>
-__global__ __launch_bounds__(256) void k_combine(const char* __restrict__ y,
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
                                                  const int32_t* __restrict__ inv_pos,
                                                  const float* __restrict__ w, int k, int d,
                                                  char* __restrict__ out) {
-  constexpr int ES = ACT == ACT_BF16 ? 2 : 4;
-  constexpr int VEC = 16 / ES;
+  constexpr int VEC = ACT == ACT_BF16 ? 8 : 4;  // one 16-byte output store
   const int64_t t = blockIdx.x;
   const int32_t* ip = inv_pos + t * k;
   const float* wt = w + t * k;
@@ -27,40 +27,35 @@ __global__ __launch_bounds__(256) void k_combine(const char* __restrict__ y,
     for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
     for (int j = 0; j < k; ++j) {
       const float wj = wt[j];
-      const u32x4 r = ld16(y + ((int64_t)ip[j] * d + c0) * ES);
-      if constexpr (ACT == ACT_BF16) {
+      const float* row = y + (int64_t)ip[j] * d + c0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += wj * bf16_bits_to_f32(r[q] & 0xFFFFu);
-          acc[2 * q + 1] += wj * bf16_bits_to_f32(r[q] >> 16);
-        }
-      } else {
+      for (int h = 0; h < VEC / 4; ++h) {
+        const u32x4 r = ld16(row + 4 * h);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] += wj * __uint_as_float(r[q]);
+        for (int q = 0; q < 4; ++q) acc[4 * h + q] += wj * __uint_as_float(r[q]);
       }
     }
     u32x4 o;
     if constexpr (ACT == ACT_BF16) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+      st16(out + (t * d + c0) * 2, o);
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
+      st16(out + (t * d + c0) * 4, o);
     }
-    st16(out + (t * d + c0) * ES, o);
   }
 }
 
-hipError_t launch_combine(int act, const void* y, const int32_t* inv_pos, const float* w, int T,
+hipError_t launch_combine(int act, const float* y, const int32_t* inv_pos, const float* w, int T,
                           int k, int d, void* out, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (act == ACT_BF16)
-    hipLaunchKernelGGL(k_combine<ACT_BF16>, dim3(T), dim3(256), 0, st,
-                       reinterpret_cast<const char*>(y), inv_pos, w, k, d,
+    hipLaunchKernelGGL(k_combine<ACT_BF16>, dim3(T), dim3(256), 0, st, y, inv_pos, w, k, d,
                        reinterpret_cast<char*>(out));
   else
-    hipLaunchKernelGGL(k_combine<ACT_F32>, dim3(T), dim3(256), 0, st,
-                       reinterpret_cast<const char*>(y), inv_pos, w, k, d,
+    hipLaunchKernelGGL(k_combine<ACT_F32>, dim3(T), dim3(256), 0, st, y, inv_pos, w, k, d,
                        reinterpret_cast<char*>(out));
   return hipGetLastError();
 }

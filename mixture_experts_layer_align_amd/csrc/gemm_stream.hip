@@ -28,7 +28,11 @@
 //   * the epilogue runs on the fp32 accumulators before the single store:
 //     SiLU(gate) * up for the concatenated gate|up weight ("La fusion de
 //     noyaux", section 4.2, GEMM + epilogue and the SwiGLU concatenation), and
-//     the fp8 per-column scale, applied after the dot product.
+//     the fp8 per-column scale, applied after the dot product.  h is stored in
+//     the activation dtype (its rounding errors average out over the down
+//     GEMM's K); the down GEMM's per-slot outputs are stored in fp32, because
+//     each output element adds k of them directly and a bf16 rounding there
+//     would stack on the output's own.
 //
 // fp8 (OCP e4m3fn) weights are converted exactly to bf16 in registers and run
 // on the same bf16 MFMA (activations stay bf16).  fp32 weights use
@@ -362,9 +366,11 @@ __global__ __launch_bounds__(64) void k_stream_gemm(const StreamGemmArgs p) {
           if (has_s1) v1[j] *= sd[SW + j];
         }
       }
-      char* dst = reinterpret_cast<char*>(p.out) + (prow * p.out_ld + ocol0) * ASZ;
-      store_chunk<ACT>(dst, v0, NV);
-      if (has_s1) store_chunk<ACT>(dst + SW * ASZ, v1, NV);
+      // per-slot expert outputs stay fp32: the combine sums them without a
+      // second rounding before the output's own
+      char* dst = reinterpret_cast<char*>(p.out) + (prow * p.out_ld + ocol0) * 4;
+      store_chunk<ACT_F32>(dst, v0, NV);
+      if (has_s1) store_chunk<ACT_F32>(dst + SW * 4, v1, NV);
     } else {
       float* dst = reinterpret_cast<float*>(p.out) + split * p.out_split_stride + prow * p.out_ld;
 #pragma unroll

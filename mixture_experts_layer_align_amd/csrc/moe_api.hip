@@ -118,13 +118,14 @@ hipError_t run_router(RouterPlan& r, int act, float* partial, const float* bias,
                      zero_n, st);
 }
 
-int validate_route(const void* x, const void* w_router, int T, int d, int E, int k, int act) {
+// Shapes and dtypes; data pointers are checked only when work is enqueued
+// (a workspace query needs none).
+int validate_route(int T, int d, int E, int k, int act) {
   if (T < 0 || d <= 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID;
   if (k > E || E > MOE_MAX_EXPERTS) return MOE_ERR_INVALID;
   if ((int64_t)T * k >= MAX_ENTRIES) return MOE_ERR_INVALID;
   if (act != MOE_F32 && act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d % 64 != 0) return MOE_ERR_UNSUPPORTED;
-  if (T > 0 && (x == nullptr || w_router == nullptr)) return MOE_ERR_INVALID;
   return MOE_OK;
 }
 
@@ -155,9 +156,8 @@ int64_t moe_align_capacity(int T, int E, int k, int bm) {
 int moe_route(const void* x, const void* w_router, const float* logit_bias, int T, int d, int E,
               int k, int act_dtype, float* logits, int32_t* topk_ids, float* topk_w,
               void* workspace, size_t* workspace_bytes, void* stream) {
-  int rc = validate_route(x, w_router, T, d, E, k, act_dtype);
+  int rc = validate_route(T, d, E, k, act_dtype);
   if (rc != MOE_OK) return rc;
-  if (T > 0 && (topk_ids == nullptr || topk_w == nullptr)) return MOE_ERR_INVALID;
   const int act = act_code(act_dtype);
   RouterPlan r = plan_router(x, w_router, T, d, E, act);
   Carve c(workspace);
@@ -165,6 +165,8 @@ int moe_route(const void* x, const void* w_router, const float* logit_bias, int 
   bool query;
   rc = check_ws(workspace, workspace_bytes, c.off, &query);
   if (rc != MOE_OK || query || T == 0) return rc;
+  if (x == nullptr || w_router == nullptr || topk_ids == nullptr || topk_w == nullptr)
+    return MOE_ERR_INVALID;
   int kidx = 0;
   hipError_t e = run_router(r, act, partial, logit_bias, T, E, k, logits, topk_ids, topk_w,
                             nullptr, 0, static_cast<hipStream_t>(stream), nullptr, &kidx);
@@ -179,14 +181,14 @@ int moe_align(const int32_t* topk_ids, int T, int E, int k, int block_m, int32_t
     return MOE_ERR_INVALID;
   const int64_t n = (int64_t)T * k;
   if (n >= MAX_ENTRIES) return MOE_ERR_INVALID;
-  if (T > 0 && (topk_ids == nullptr || expert_counts == nullptr || padded_offsets == nullptr ||
-                sorted_ids == nullptr || inv_pos == nullptr || block_expert == nullptr))
-    return MOE_ERR_INVALID;
   const int64_t need = align_workspace_bytes((int)n, E);
   bool query;
   int rc = check_ws(workspace, workspace_bytes, need, &query);
   if (rc != MOE_OK || query) return rc;
   if (T == 0) return MOE_OK;
+  if (topk_ids == nullptr || expert_counts == nullptr || padded_offsets == nullptr ||
+      sorted_ids == nullptr || inv_pos == nullptr || block_expert == nullptr)
+    return MOE_ERR_INVALID;
   AlignArgs a{};
   a.ids = topk_ids;
   a.n = (int)n;
@@ -209,7 +211,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
                        void* stream) {
   if (L == nullptr) return MOE_ERR_INVALID;
   const int d = L->d, dff = L->d_ff, E = L->E, k = L->k;
-  int rc = validate_route(x, L->w_router, T, d, E, k, L->act_dtype);
+  int rc = validate_route(T, d, E, k, L->act_dtype);
   if (rc != MOE_OK) return rc;
   if (dff <= 0) return MOE_ERR_INVALID;
   if (d % 128 != 0 || dff % 128 != 0) return MOE_ERR_UNSUPPORTED;
@@ -217,11 +219,8 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
                        (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_BF16) ||
                        (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_FP8_E4M3);
   if (!pair_ok) return MOE_ERR_UNSUPPORTED;
-  if (T > 0 && (L->w_gate_up == nullptr || L->w_down == nullptr || out == nullptr))
-    return MOE_ERR_INVALID;
   if (L->w_dtype == MOE_FP8_E4M3 && (L->scale_gate_up == nullptr || L->scale_down == nullptr))
     return MOE_ERR_INVALID;
-  if (T > 0 && out == x) return MOE_ERR_INVALID;
 
   const int act = act_code(L->act_dtype);
   const int wdt = w_code(L->w_dtype);
@@ -261,7 +260,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   int32_t* bexp = c.take<int32_t>(std::max<int64_t>(nblocks, 1));
   char* al_ws = c.take<char>(std::max<int64_t>(align_workspace_bytes((int)n, E), 1));
   char* h = c.take<char>(std::max<int64_t>(cap * dff * ab, 1));
-  char* y = c.take<char>(std::max<int64_t>(cap * d * ab, 1));
+  float* y = c.take<float>(std::max<int64_t>(cap * d, 1));
   float* gpart = c.take<float>(std::max<int64_t>(std::max(gu_partial, dn_partial), 1));
   int32_t* counters = c.take<int32_t>(std::max<int64_t>(ncounters, 1));
   bool query;
@@ -270,6 +269,9 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   if (routing != nullptr && routing->block_m != nullptr) *routing->block_m = bm;
   if (tr != nullptr) tr->n_kernels = 0;
   if (T == 0) return MOE_OK;
+  if (x == nullptr || out == nullptr || L->w_router == nullptr || L->w_gate_up == nullptr ||
+      L->w_down == nullptr || out == x)
+    return MOE_ERR_INVALID;
 
   // routing views the caller asked for are written in place
   if (routing != nullptr) {

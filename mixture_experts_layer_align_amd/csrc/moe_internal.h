@@ -23,7 +23,7 @@ enum { A_DENSE = 0,    // row p = input row p, valid when p < m_total
        A_PADDED = 2 }; // row p = input row p, valid when sorted_ids[p] >= 0
 
 enum { EPI_SILU_MUL = 0,  // two slabs (gate, up) -> act dtype  h = silu(g)*u
-       EPI_STORE = 1,     // two adjacent slabs -> act dtype
+       EPI_STORE = 1,     // two adjacent slabs -> fp32
        EPI_F32 = 2 };     // two adjacent slabs -> fp32, no reduction; split s
                           // writes its own [m_total, ld] plane
 
@@ -102,7 +102,8 @@ hipError_t launch_align(AlignArgs a, void* ws, hipStream_t st);
 
 // ------------------------------------------------------------ combine
 
-hipError_t launch_combine(int act_dtype, const void* y, const int32_t* inv_pos, const float* w,
+// y: per-slot expert outputs, fp32 [cap, d]
+hipError_t launch_combine(int act_dtype, const float* y, const int32_t* inv_pos, const float* w,
                           int T, int k, int d, void* out, hipStream_t st);
 
 }  // namespace moe

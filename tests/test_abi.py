@@ -66,8 +66,8 @@ def test_route_validation_errors_before_any_launch():
     assert _route(T=-1)[0] == B.MOE_ERR_INVALID
     assert _route(d=100)[0] == B.MOE_ERR_UNSUPPORTED
     assert _route(act=B.MOE_FP8_E4M3)[0] == B.MOE_ERR_UNSUPPORTED
-    assert _route(x=0)[0] == B.MOE_ERR_INVALID
-    rc, need = _route()
+    assert _route(x=0, ws=ctypes.c_void_p(4096))[0] in (B.MOE_ERR_INVALID, B.MOE_ERR_WORKSPACE)
+    rc, need = _route(x=0, w=0, ids=0, tw=0)          # a query needs no data pointers
     assert rc == B.MOE_OK and need > 0          # workspace query
     assert _route(T=0, x=0, w=0, ids=0, tw=0)[0] == B.MOE_OK
 
@@ -86,8 +86,9 @@ def test_align_validation_errors():
     assert n.value == 0                                             # one workgroup, no scratch
     assert lib.moe_align(*args(3000, 8, 2, 32)) == B.MOE_OK
     assert n.value > 0                                              # multi-tile scratch
-    assert lib.moe_align(None, 4, 8, 2, 32, p, p, p, p, p, None, ctypes.byref(n), None) \
-        == B.MOE_ERR_INVALID
+    n.value = 0
+    assert lib.moe_align(None, 4, 8, 2, 32, p, p, p, p, p, vp(4096), ctypes.byref(n), None) \
+        == B.MOE_ERR_INVALID                                        # data pointer missing
 
 
 def _layer(**kw):
@@ -118,7 +119,7 @@ def test_forward_validation_and_workspace_query():
     assert _fwd(_layer(wdt=B.MOE_FP8_E4M3))[0] == B.MOE_ERR_INVALID     # scales missing
     assert _fwd(_layer(wdt=B.MOE_FP8_E4M3, sgu=1, sdn=1))[0] == B.MOE_OK
     assert _fwd(_layer(k=9))[0] == B.MOE_ERR_INVALID
-    assert _fwd(_layer(), x=8, out=8)[0] == B.MOE_ERR_INVALID           # out aliases x
+    assert _fwd(_layer(), x=0, out=0)[0] == B.MOE_OK                    # query: no data
     # a given workspace smaller than the requirement is refused before any launch
     _, need = _fwd(_layer(), T=64)
     assert need > 0
