@@ -76,7 +76,7 @@ def main():
     # per-kernel durations, HIP events recorded on the launch stream between
     # the kernels of each forward
     rb = fwd.routing_buffers(T)
-    _, bm, names = fwd(x, routing=rb)
+    _, bm, names = fwd(x, routing=rb, events=[])
     torch.cuda.synchronize()
     nk = len(names)
     ev = B.HipEvents(nk + 1)

@@ -1,0 +1,384 @@
+// Weight-streaming grouped expert GEMM for thin token blocks (decode regime).
+//
+// Expert compute is A[M,K] x B[K,N] -> C[M,N] with M token rows, K the hidden
+// size and N the expert's output width (vLLM fused-MoE post, section
+// "Swap-AB"); B is the expert weight stored [K, N], N contiguous.  With few
+// rows per expert the cost is streaming B from HBM once (the decode case of
+// "CuTeDSL at Perplexity", section on prefill and decode: DRAM loads of
+// weights dominate).  The pages' Hopper answer is to swap operands so the
+// large N fills the fixed 64-row side of the tensor-core instruction.  The
+// gfx950 version of that idea:
+//
+//   * the weight panel is the MFMA A operand (rows = output columns n) and the
+//     tokens the B operand (columns = rows of the block), so
+//     v_mfma_f32_16x16x32_bf16 produces 16 output columns x 16 tokens;
+//   * a workgroup owns (32-row block of one expert, n-tile, k-range); each of
+//     its two waves streams one slab of the tile (for gate|up: the gate slab
+//     and the matching up slab), applying every weight fragment to all rows of
+//     the block (weight-stationary); a 16-row group with no routed row is
+//     skipped;
+//   * weights go HBM -> LDS with direct loads (global_load_lds_dwordx4: no
+//     VGPR holds data in flight) through a 4-stage ring per wave, 8 KB a stage;
+//     each lane reads back exactly the 16-byte chunks it requested (8
+//     consecutive weight rows, 16 lanes covering 256 contiguous bytes of a row)
+//     and transposes its 8x8 bf16 block in registers (v_perm_b32) into 8 MFMA A
+//     fragments; the wait before each stage is an explicit vmcnt that leaves
+//     the later stages in flight;
+//   * tokens are gathered straight from x by the aligned slot list, so the
+//     permuted activations are never materialised (the pages copy tokens into
+//     padded per-expert buffers first: "CuTeDSL at Perplexity", MoE dispatch
+//     and combine, local kernel);
+//   * when blocks x n-tiles cannot fill the chip, K is split; each split stores
+//     an fp32 partial and the last split to finish (an integer counter decides
+//     who, not what) sums all partials in split order, so results do not
+//     depend on scheduling;
+//   * the epilogue runs on the fp32 accumulators before the single store:
+//     SiLU(gate) * up for the concatenated gate|up weight ("La fusion de
+//     noyaux", section 4.2, GEMM + epilogue and the SwiGLU concatenation), and
+//     the fp8 per-column scale, applied after the dot product.  h is stored in
+//     the activation dtype (its rounding errors average out over the down
+//     GEMM's K); the down GEMM's per-slot outputs are stored in fp32, because
+//     each output element adds k of them directly and a bf16 rounding there
+//     would stack on the output's own.
+//
+// fp8 (OCP e4m3fn) weights: a lane loads 16 codes of a row (slabs of 256
+// columns), converts them exactly to bf16 in registers and runs the same bf16
+// MFMA (activations stay bf16).  fp32 weights: 4 columns per lane, no
+// transpose, v_mfma_f32_16x16x4_f32.
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+template <int WT>
+struct DTr;
+template <>
+struct DTr<W_BF16> {
+  static constexpr int CPL = 8;     // weight columns per lane
+  static constexpr int RPL = 8;     // weight rows per lane per k-step (one 16 B load each)
+  static constexpr int KSTEP = 32;
+  static constexpr int ESIZE = 2;
+};
+template <>
+struct DTr<W_FP8> {
+  static constexpr int CPL = 16;
+  static constexpr int RPL = 8;
+  static constexpr int KSTEP = 32;
+  static constexpr int ESIZE = 1;
+};
+template <>
+struct DTr<W_F32> {
+  static constexpr int CPL = 4;
+  static constexpr int RPL = 4;
+  static constexpr int KSTEP = 16;
+  static constexpr int ESIZE = 4;
+};
+
+constexpr int STAGES = 4;
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
+// operations of this wave are outstanding; LDS/scalar and export counters are
+// left alone.
+constexpr int vmcnt_imm(int n) {
+  return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14);
+}
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+
+}  // namespace
+
+template <int ACT, int WT, int EPI>
+__global__ __launch_bounds__(128) void k_expert_stream(const StreamGemmArgs p) {
+  using Tr = DTr<WT>;
+  constexpr int CPL = Tr::CPL;
+  constexpr int RPL = Tr::RPL;
+  constexpr int KSTEP = Tr::KSTEP;
+  constexpr int SW = 16 * CPL;    // slab width (weight columns per wave)
+  constexpr int NV = 4 * CPL;     // contiguous output columns per lane
+  constexpr int ASZ = (ACT == ACT_BF16) ? 2 : 4;
+  constexpr int XK = (ACT == ACT_BF16) ? 8 : 4;  // k-values per lane per token fragment
+  constexpr int S = STAGES;
+  constexpr int PER = RPL + 2;    // vector-memory ops per stage: weight rows + 2 token loads
+  static_assert((S - 1) * PER <= 63, "vmcnt field");
+
+  // ring[wave][stage][row][lane]; after the main loop the same memory holds
+  // the split-K flag and the epilogue exchange
+  __shared__ u32x4 lds[2 * S * RPL * WAVE];
+
+  const int lane = threadIdx.x & 63;
+  const int slab = threadIdx.x >> 6;
+  const int li = lane & 15;  // MFMA column within a 16-group (token row)
+  const int lg = lane >> 4;  // k group
+
+  int id = blockIdx.x;
+  const int split = id % p.ksplit;
+  id /= p.ksplit;
+  const int nt = id % p.n_tiles;
+  const int mb = id / p.n_tiles;
+  const int e = p.block_expert[mb];
+  if (e < 0) return;  // whole workgroup: a block past the routed rows
+  const int p0 = mb * STREAM_BM;
+
+  // -------------------------------------------------------- token rows
+  const char* arow[2];
+  bool rvalid[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int prow = p0 + 16 * q + li;
+    const int sid = p.sorted_ids[prow];
+    rvalid[q] = sid >= 0;
+    int64_t src = 0;  // invalid rows read row 0 (in bounds) and are zeroed
+    if (rvalid[q]) src = (p.a_mode == A_GATHER) ? sid / p.topk : prow;
+    arow[q] = reinterpret_cast<const char*>(p.a) + src * p.a_ld * ASZ;
+  }
+  const bool use_q1 = ballot(rvalid[1]) != 0;
+
+  // -------------------------------------------------------- weight columns
+  int wcol, ocol;  // this lane's first weight column; first output column
+  if constexpr (EPI == EPI_SILU_MUL) {
+    wcol = (slab ? p.up_off : 0) + nt * SW + CPL * li;
+    ocol = nt * SW + lg * NV;
+  } else {
+    wcol = nt * 2 * SW + slab * SW + CPL * li;
+    ocol = nt * 2 * SW + slab * SW + lg * NV;
+  }
+  // the second slab of the last down tile may lie past the output width
+  const bool active = (EPI != EPI_STORE) || (nt * 2 * SW + slab * SW < p.n_out);
+  const int64_t wrow_bytes = p.w_ld * Tr::ESIZE;
+  const int kb = split * p.kchunk;
+  const int ke = min(p.K, kb + p.kchunk);
+  const int nsteps = (ke - kb) / KSTEP;
+  const char* wbase = reinterpret_cast<const char*>(p.w) + (int64_t)e * p.w_estride * Tr::ESIZE +
+                      (int64_t)(kb + lg * RPL) * wrow_bytes + (int64_t)wcol * Tr::ESIZE;
+  u32x4* ring = lds + slab * S * RPL * WAVE;
+
+  f32x4 acc[2][CPL];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[q][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (active && nsteps > 0) {
+    u32x4 xb[S][2];
+    // stage s <- k-step `step` (clamped: steps past the end reload the last)
+    auto issue = [&](int s, int step) {
+      const int sc = min(step, nsteps - 1);
+      const char* src = wbase + (int64_t)sc * KSTEP * wrow_bytes;
+#pragma unroll
+      for (int j = 0; j < RPL; ++j) dma16(src + j * wrow_bytes, ring + (s * RPL + j) * WAVE);
+      const int64_t kk = (int64_t)(kb + sc * KSTEP + XK * lg) * ASZ;
+      xb[s][0] = ld16(arow[0] + kk);
+      xb[s][1] = ld16(arow[1] + kk);
+    };
+    auto compute = [&](int s) {
+      u32x4 raw[RPL];
+#pragma unroll
+      for (int j = 0; j < RPL; ++j) raw[j] = ring[(s * RPL + j) * WAVE + lane];
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const u32x4 x0 = rvalid[0] ? xb[s][0] : z;
+      const u32x4 x1 = rvalid[1] ? xb[s][1] : z;
+      if constexpr (WT == W_F32) {
+#pragma unroll
+        for (int ss = 0; ss < 4; ++ss)
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const float a = __uint_as_float(raw[ss][c]);
+            acc[0][c] = mfma_f32_16x16x4(a, __uint_as_float(x0[ss]), acc[0][c]);
+            if (use_q1) acc[1][c] = mfma_f32_16x16x4(a, __uint_as_float(x1[ss]), acc[1][c]);
+          }
+      } else if constexpr (WT == W_BF16) {
+        u32x4 frag[8];
+        transpose8x8_b16(raw, frag);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          acc[0][c] = mfma_bf16_16x16x32(frag[c], x0, acc[0][c]);
+          if (use_q1) acc[1][c] = mfma_bf16_16x16x32(frag[c], x1, acc[1][c]);
+        }
+      } else {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          u32x4 rows[8], frag[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            rows[j] = fp8x8_to_bf16x8(half ? u32x2{raw[j][2], raw[j][3]} : u32x2{raw[j][0], raw[j][1]});
+          transpose8x8_b16(rows, frag);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            acc[0][8 * half + c] = mfma_bf16_16x16x32(frag[c], x0, acc[0][8 * half + c]);
+            if (use_q1) acc[1][8 * half + c] = mfma_bf16_16x16x32(frag[c], x1, acc[1][8 * half + c]);
+          }
+        }
+      }
+    };
+#pragma unroll
+    for (int s = 0; s < S; ++s) issue(s, s);
+    for (int it = 0; it < nsteps; it += S) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        // stage s complete: only the S-1 later stages may still be in flight
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * PER));
+        __builtin_amdgcn_sched_barrier(0);
+        if (it + s < nsteps) compute(s);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(s, it + s + S);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+  __syncthreads();  // the ring is free from here on
+
+  // -------------------------------------------------------- split-K reduction
+  int* s_last = reinterpret_cast<int*>(lds);
+  if (p.ksplit > 1) {
+    const int64_t tile = (int64_t)mb * p.n_tiles + nt;
+    constexpr int64_t PFW = (int64_t)2 * CPL * 4 * WAVE;  // floats per wave partial
+    float* part = p.partial + tile * p.ksplit * 2 * PFW;
+    float* mine = part + ((int64_t)split * 2 + slab) * PFW;
+    if (active) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        if (rvalid[q])
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+            *reinterpret_cast<f32x4*>(mine + ((int64_t)(q * CPL + c) * WAVE + lane) * 4) = acc[q][c];
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      *s_last = atomicAdd(p.counters + tile, 1);
+      __threadfence();
+    }
+    __syncthreads();
+    if (*s_last != p.ksplit - 1) return;  // uniform over the workgroup
+    __threadfence();
+    if (active) {
+      f32x4 sum[2][CPL];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) sum[q][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int sp = 0; sp < p.ksplit; ++sp) {
+        const float* src = part + ((int64_t)sp * 2 + slab) * PFW;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          if (rvalid[q])
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+              const f32x4 v = (sp == split) ? acc[q][c]
+                                            : *reinterpret_cast<const f32x4*>(
+                                                  src + ((int64_t)(q * CPL + c) * WAVE + lane) * 4);
+              sum[q][c] += v;
+            }
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[q][c] = sum[q][c];
+    }
+    if (threadIdx.x == 0) p.counters[tile] = 0;
+    __syncthreads();  // s_last read by all before the exchange reuses the memory
+  }
+
+  // -------------------------------------------------------- epilogue
+  // Lane (li, lg) holds, for row group q, output columns ocol + j with
+  // j = r*CPL + c in acc[q][c][r].
+  if constexpr (EPI == EPI_SILU_MUL) {
+    if (WT == W_FP8) {
+      const float* sc = p.scale + (int64_t)e * p.scale_estride + (slab ? p.up_off : 0) + ocol;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const float f = sc[r * CPL + c];
+          acc[0][c][r] *= f;
+          acc[1][c][r] *= f;
+        }
+    }
+    // wave 0 (gate) finishes row group 0 and wave 1 (up) row group 1; each
+    // hands the other the accumulators of the group it does not finish
+    // (selects, not indexing by the wave number, keep acc in registers)
+    f32x4* xch = reinterpret_cast<f32x4*>(lds);  // [2][CPL][WAVE]
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) xch[(slab * CPL + c) * WAVE + lane] = slab ? acc[0][c] : acc[1][c];
+    __syncthreads();
+    const int keep = slab;
+    if (!rvalid[keep]) return;
+    const int64_t prow = p0 + 16 * keep + li;
+    float h[NV];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const f32x4 mine = slab ? acc[1][c] : acc[0][c];
+      const f32x4 other = xch[((1 - slab) * CPL + c) * WAVE + lane];
+      const f32x4 g = slab ? other : mine;
+      const f32x4 u = slab ? mine : other;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h[r * CPL + c] = silu(g[r]) * u[r];
+    }
+    char* dst = reinterpret_cast<char*>(p.out) + (prow * p.out_ld + ocol) * ASZ;
+    store_act<ACT>(dst, h, NV);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (!active || !rvalid[q]) continue;
+      const int64_t prow = p0 + 16 * q + li;
+      float v[NV];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[r * CPL + c] = acc[q][c][r];
+      if (WT == W_FP8) {
+        const float* sd = p.scale + (int64_t)e * p.scale_estride + ocol;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) v[j] *= sd[j];
+      }
+      // per-slot expert outputs stay fp32
+      char* dst = reinterpret_cast<char*>(p.out) + (prow * p.out_ld + ocol) * 4;
+      store_act<ACT_F32>(dst, v, NV);
+    }
+  }
+}
+
+int stream_tile_cols(int w_dtype, int epi) {
+  const int sw = 16 * (w_dtype == W_F32 ? DTr<W_F32>::CPL
+                                         : (w_dtype == W_FP8 ? DTr<W_FP8>::CPL : DTr<W_BF16>::CPL));
+  return epi == EPI_SILU_MUL ? sw : 2 * sw;
+}
+
+int stream_kstep(int w_dtype) {
+  return (w_dtype == W_F32) ? DTr<W_F32>::KSTEP : DTr<W_BF16>::KSTEP;
+}
+
+int64_t stream_partial_floats_per_tile_split(int w_dtype) {
+  const int cpl = w_dtype == W_F32 ? DTr<W_F32>::CPL
+                                   : (w_dtype == W_FP8 ? DTr<W_FP8>::CPL : DTr<W_BF16>::CPL);
+  return (int64_t)2 * 2 * cpl * 4 * WAVE;
+}
+
+template <int ACT, int WT, int EPI>
+static hipError_t launch_one(const StreamGemmArgs& a, hipStream_t st) {
+  const int64_t grid = (int64_t)a.num_mblocks * a.n_tiles * a.ksplit;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_expert_stream<ACT, WT, EPI>), dim3((unsigned)grid), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_gemm(int act, int wdt, int epi, const StreamGemmArgs& a, hipStream_t st) {
+#define MOE_CASE(A_, W_, E_) \
+  if (act == A_ && wdt == W_ && epi == E_) return launch_one<A_, W_, E_>(a, st);
+  MOE_CASE(ACT_F32, W_F32, EPI_SILU_MUL)
+  MOE_CASE(ACT_F32, W_F32, EPI_STORE)
+  MOE_CASE(ACT_BF16, W_BF16, EPI_SILU_MUL)
+  MOE_CASE(ACT_BF16, W_BF16, EPI_STORE)
+  MOE_CASE(ACT_BF16, W_FP8, EPI_SILU_MUL)
+  MOE_CASE(ACT_BF16, W_FP8, EPI_STORE)
+#undef MOE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -11,7 +11,8 @@ using namespace moe;
 namespace {
 
 constexpr int64_t WS_ALIGN = 256;
-constexpr int TARGET_WAVES = 2048;   // waves worth launching at once (8 per CU)
+constexpr int TARGET_WGS = 512;      // two-wave workgroups resident at once (2 per CU)
+constexpr int ROUTER_MAX_SPLIT = 16;
 constexpr int64_t MAX_ENTRIES = int64_t(1) << 24;
 
 int64_t up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -48,13 +49,16 @@ int check_ws(void* ws, size_t* ws_bytes, int64_t need, bool* query) {
   return MOE_OK;
 }
 
-// Split K so that items * split waves approach TARGET_WAVES, keeping at least
-// two k-steps per split.  Returns the k-chunk (a multiple of kstep).
-int choose_kchunk(int64_t items, int K, int kstep, int* nsplit) {
+// Split K so that items * split workgroups approach TARGET_WGS, keeping at
+// least two k-steps per split and at most max_split splits.  Returns the
+// k-chunk (a multiple of kstep).
+int choose_kchunk(int64_t items, int K, int kstep, int* nsplit, int max_split = 1 << 20) {
   const int steps = K / kstep;
   items = std::max<int64_t>(items, 1);
   int s = 1;
-  if (items < TARGET_WAVES) s = (int)std::min<int64_t>((TARGET_WAVES + items - 1) / items, steps / 2);
+  if (items < TARGET_WGS)
+    s = (int)std::min<int64_t>({(TARGET_WGS + items - 1) / items, (int64_t)steps / 2,
+                                (int64_t)max_split});
   s = std::max(s, 1);
   const int chunk_steps = (steps + s - 1) / s;
   *nsplit = (steps + chunk_steps - 1) / chunk_steps;
@@ -70,7 +74,6 @@ struct RouterPlan {
 
 RouterPlan plan_router(const void* x, const void* w_router, int T, int d, int E, int act) {
   RouterPlan r{};
-  const int wdt = (act == ACT_BF16) ? W_BF16 : W_F32;
   StreamGemmArgs& g = r.g;
   g.a = x;
   g.a_ld = d;
@@ -83,9 +86,10 @@ RouterPlan plan_router(const void* x, const void* w_router, int T, int d, int E,
   g.w_estride = 0;
   g.K = d;
   g.n_out = E;
-  const int tc = stream_tile_cols(wdt, EPI_F32);
+  const int tc = router_tile_cols(act);
   g.n_tiles = (E + tc - 1) / tc;
-  g.kchunk = choose_kchunk((int64_t)g.num_mblocks * g.n_tiles, d, stream_kstep(wdt), &g.ksplit);
+  g.kchunk = choose_kchunk((int64_t)g.num_mblocks * g.n_tiles, d, router_kstep(act), &g.ksplit,
+                           ROUTER_MAX_SPLIT);
   g.out_ld = E;
   g.out_split_stride = (int64_t)T * E;
   r.nsplit = g.ksplit;
@@ -111,7 +115,7 @@ hipError_t run_router(RouterPlan& r, int act, float* partial, const float* bias,
                       int64_t zero_n, hipStream_t st, moe_trace* tr, int* kidx) {
   r.g.out = partial;
   trace_mark(tr, kidx, "router_gemm", st);
-  hipError_t e = launch_stream_gemm(act, act == ACT_BF16 ? W_BF16 : W_F32, EPI_F32, r.g, st);
+  hipError_t e = launch_router_gemm(act, r.g, st);
   if (e != hipSuccess) return e;
   trace_mark(tr, kidx, "topk", st);
   return launch_topk(partial, r.nsplit, (int64_t)T * E, bias, T, E, k, logits, ids, w, zero_ptr,
@@ -219,6 +223,8 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
                        (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_BF16) ||
                        (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_FP8_E4M3);
   if (!pair_ok) return MOE_ERR_UNSUPPORTED;
+  // fp8 expert slabs are 256 columns wide
+  if (L->w_dtype == MOE_FP8_E4M3 && (d % 256 != 0 || dff % 256 != 0)) return MOE_ERR_UNSUPPORTED;
   if (L->w_dtype == MOE_FP8_E4M3 && (L->scale_gate_up == nullptr || L->scale_down == nullptr))
     return MOE_ERR_INVALID;
 

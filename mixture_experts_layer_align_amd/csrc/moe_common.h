@@ -105,6 +105,28 @@ __device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// nv values (multiple of 8 for bf16, 4 for fp32) to a 16-byte aligned
+// destination in the activation dtype, rounding to nearest even for bf16.
+template <int ACT_IS_BF16>
+__device__ __forceinline__ void store_act(char* dst, const float* v, int nv) {
+  if constexpr (ACT_IS_BF16 == 1) {
+    for (int j = 0; j < nv; j += 8) {
+      u32x4 o;
+      o[0] = pack_bf16x2(v[j + 0], v[j + 1]);
+      o[1] = pack_bf16x2(v[j + 2], v[j + 3]);
+      o[2] = pack_bf16x2(v[j + 4], v[j + 5]);
+      o[3] = pack_bf16x2(v[j + 6], v[j + 7]);
+      st16(dst + j * 2, o);
+    }
+  } else {
+    for (int j = 0; j < nv; j += 4) {
+      u32x4 o = {__float_as_uint(v[j]), __float_as_uint(v[j + 1]), __float_as_uint(v[j + 2]),
+                 __float_as_uint(v[j + 3])};
+      st16(dst + j * 4, o);
+    }
+  }
+}
+
 // ------------------------------------------------------------ activation
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }

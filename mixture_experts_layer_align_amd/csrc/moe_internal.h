@@ -11,21 +11,20 @@ constexpr int MAX_EXPERTS = 1024;
 enum { ACT_F32 = 0, ACT_BF16 = 1 };             // activation storage
 enum { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };      // expert-weight storage
 
-// ------------------------------------------------------------ stream GEMM
+// ------------------------------------------------------------ stream GEMMs
 //
-// Weight-streaming grouped GEMM: one wave per work item (m-block of 32 rows,
-// n-tile, k-split).  Every wave streams its [k-range, n-tile] panel of one
-// expert's weight once, straight from HBM into registers, and multiplies it
-// with all rows of its block.
+// Weight-streaming GEMMs: one two-wave workgroup per work item (m-block of 32
+// rows, n-tile, k-split).  Every wave streams one column slab of its k-range
+// once and multiplies it with all rows of its block.  The expert GEMMs stage
+// weights through LDS with direct loads; the router GEMM (N = E, any width)
+// stages them in registers.
 
 enum { A_DENSE = 0,    // row p = input row p, valid when p < m_total
        A_GATHER = 1,   // row p = input row sorted_ids[p] / topk, valid when >= 0
        A_PADDED = 2 }; // row p = input row p, valid when sorted_ids[p] >= 0
 
 enum { EPI_SILU_MUL = 0,  // two slabs (gate, up) -> act dtype  h = silu(g)*u
-       EPI_STORE = 1,     // two adjacent slabs -> fp32
-       EPI_F32 = 2 };     // two adjacent slabs -> fp32, no reduction; split s
-                          // writes its own [m_total, ld] plane
+       EPI_STORE = 1 };   // two adjacent slabs -> fp32
 
 struct StreamGemmArgs {
   const void* a;          // row source
@@ -51,7 +50,7 @@ struct StreamGemmArgs {
   int32_t* counters;      // one per (m-block, n-tile), zero on entry
   void* out;
   int64_t out_ld;
-  int64_t out_split_stride;  // EPI_F32: elements between split planes
+  int64_t out_split_stride;  // router: elements between split planes
 };
 
 // Rows per m-block of the stream GEMM (two 16-row MFMA column groups).
@@ -66,6 +65,12 @@ int64_t stream_partial_floats_per_tile_split(int w_dtype);
 
 hipError_t launch_stream_gemm(int act_dtype, int w_dtype, int epi, const StreamGemmArgs& a,
                               hipStream_t st);
+
+// Router logits: A_DENSE rows, weights [K, n_out] with any n_out; split s writes
+// the fp32 plane out + s * out_split_stride.
+int router_tile_cols(int act_dtype);
+int router_kstep(int act_dtype);
+hipError_t launch_router_gemm(int act_dtype, const StreamGemmArgs& a, hipStream_t st);
 
 // ------------------------------------------------------------ routing
 

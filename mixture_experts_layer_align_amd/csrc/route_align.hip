@@ -60,6 +60,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial,
     if (e < E) {
       const float* pp = partial + (int64_t)t * E + e;
       s = pp[0];
+#pragma unroll 4
       for (int sp = 1; sp < nsplit; ++sp) s += pp[sp * split_stride];
       if (bias != nullptr) s += bias[e];
       if (logits != nullptr) logits[(int64_t)t * E + e] = s;
