@@ -27,6 +27,8 @@ def parse():
                     help="batch size (default: the largest decode batch of the config)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="also run a plain device copy of MB megabytes (counter calibration)")
     return ap.parse_args()
 
 
@@ -104,7 +106,7 @@ def main():
         achieved = dom_bytes / (kern[dom] * 1e-3) / 1e9
         peak = R.HBM_BYTES_PER_S / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": peak, "unit": "GB/s"}
-    roof.update({"frac": achieved / peak, "traffic": None, "kernel": dom,
+    roof.update({"frac": achieved / peak, "traffic": measured_traffic(dom, sh, T), "kernel": dom,
                  "kernel_ms": kern[dom], "algorithmic_bytes_per_launch": dom_bytes,
                  "algorithmic_flops_per_launch": dom_flops})
 
@@ -147,9 +149,39 @@ def main():
         "sweep": sweep,
     }
 
+    if args.copy_calibration:
+        # a plain copy of known size, so hardware byte counters can be scaled
+        n = args.copy_calibration * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n
+
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layer, bias, x, sh)
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(kernel, sh, T):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    record for this workload (FETCH_SIZE and WRITE_SIZE scaled by a plain copy
+    of known size), or None when there is none or the kernel's source changed
+    since the counters were taken."""
+    import glob
+    import hashlib
+    want = f"E={sh.E} top-{sh.k} d={sh.d} d_ff={sh.d_ff} {sh.wdt} T={T}"
+    for path in glob.glob(os.path.join(ROOT, "profiles", "traffic_*.json")):
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("kernel") != kernel or rec.get("workload") != want:
+            continue
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+                return None
+        return rec["traffic_bytes_per_launch"]
+    return None
 
 
 def cpu_baseline(layer, bias, x, sh):
