@@ -3,17 +3,19 @@
 // "CuTeDSL at Perplexity", MoE dispatch and combine, local kernel: combine
 // accumulates each token's expert outputs in registers, vectorised, using the
 // routing weights and the positions dispatch assigned.  Here a workgroup
-// handles one token: each thread owns 8 (bf16 output) or 4 (fp32 output)
-// consecutive elements, loads the k fp32 expert rows with 16-byte loads and
-// sums them in fp32 in slot order j = 0..k-1, then rounds once to the
-// activation dtype.
+// handles one token and a 2048- (bf16 output) or 1024-element (fp32) chunk:
+// each thread owns 8 or 4 consecutive elements, loads the k fp32 expert rows
+// with 16-byte loads (first adding a row's k-split partial sums, in split
+// order, when the down GEMM was split) and sums them in fp32 in slot order
+// j = 0..k-1, then rounds once to the activation dtype.
 #include "moe_common.h"
 #include "moe_internal.h"
 
 namespace moe {
 
 template <int ACT>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, int nsplit,
+                                                 int64_t split_stride,
                                                  const int32_t* __restrict__ inv_pos,
                                                  const float* __restrict__ w, int k, int d,
                                                  char* __restrict__ out) {
@@ -21,19 +23,27 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
   const int64_t t = blockIdx.x;
   const int32_t* ip = inv_pos + t * k;
   const float* wt = w + t * k;
-  for (int c0 = threadIdx.x * VEC; c0 < d; c0 += 256 * VEC) {
+  const int c0 = (blockIdx.y * 256 + threadIdx.x) * VEC;
+  if (c0 < d) {
     float acc[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
     for (int j = 0; j < k; ++j) {
       const float wj = wt[j];
       const float* row = y + (int64_t)ip[j] * d + c0;
+      float ys[VEC];
 #pragma unroll
-      for (int h = 0; h < VEC / 4; ++h) {
-        const u32x4 r = ld16(row + 4 * h);
+      for (int v = 0; v < VEC; ++v) ys[v] = 0.f;
+      for (int s = 0; s < nsplit; ++s) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[4 * h + q] += wj * __uint_as_float(r[q]);
+        for (int h = 0; h < VEC / 4; ++h) {
+          const u32x4 r = ld16(row + s * split_stride + 4 * h);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ys[4 * h + q] += __uint_as_float(r[q]);
+        }
       }
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[v] += wj * ys[v];
     }
     u32x4 o;
     if constexpr (ACT == ACT_BF16) {
@@ -48,15 +58,18 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
   }
 }
 
-hipError_t launch_combine(int act, const float* y, const int32_t* inv_pos, const float* w, int T,
-                          int k, int d, void* out, hipStream_t st) {
+hipError_t launch_combine(int act, const float* y, int nsplit, int64_t split_stride,
+                          const int32_t* inv_pos, const float* w, int T, int k, int d, void* out,
+                          hipStream_t st) {
   if (T == 0) return hipSuccess;
+  const int vec = act == ACT_BF16 ? 8 : 4;
+  const dim3 grid((unsigned)T, (unsigned)((d + 256 * vec - 1) / (256 * vec)));
   if (act == ACT_BF16)
-    hipLaunchKernelGGL(k_combine<ACT_BF16>, dim3(T), dim3(256), 0, st, y, inv_pos, w, k, d,
-                       reinterpret_cast<char*>(out));
+    hipLaunchKernelGGL(k_combine<ACT_BF16>, grid, dim3(256), 0, st, y, nsplit, split_stride,
+                       inv_pos, w, k, d, reinterpret_cast<char*>(out));
   else
-    hipLaunchKernelGGL(k_combine<ACT_F32>, dim3(T), dim3(256), 0, st, y, inv_pos, w, k, d,
-                       reinterpret_cast<char*>(out));
+    hipLaunchKernelGGL(k_combine<ACT_F32>, grid, dim3(256), 0, st, y, nsplit, split_stride,
+                       inv_pos, w, k, d, reinterpret_cast<char*>(out));
   return hipGetLastError();
 }
 

@@ -28,10 +28,11 @@
 //     permuted activations are never materialised (the pages copy tokens into
 //     padded per-expert buffers first: "CuTeDSL at Perplexity", MoE dispatch
 //     and combine, local kernel);
-//   * when blocks x n-tiles cannot fill the chip, K is split; each split stores
-//     an fp32 partial and the last split to finish (an integer counter decides
-//     who, not what) sums all partials in split order, so results do not
-//     depend on scheduling;
+//   * when blocks x n-tiles cannot fill the chip, K is split: each split stores
+//     fp32 partial sums and the next kernel adds them in split order (fixed
+//     order, no atomics, no device-scope fences: on gfx950 a device-scope
+//     fence writes back and invalidates the XCD's L2, which hundreds of
+//     workgroups streaming through that L2 cannot afford);
 //   * the epilogue runs on the fp32 accumulators before the single store:
 //     SiLU(gate) * up for the concatenated gate|up weight ("La fusion de
 //     noyaux", section 4.2, GEMM + epilogue and the SwiGLU concatenation), and
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(128) void k_expert_stream(const StreamGemmArgs p) {
   static_assert((S - 1) * PER <= 63, "vmcnt field");
 
   // ring[wave][stage][row][lane]; after the main loop the same memory holds
-  // the split-K flag and the epilogue exchange
+  // the epilogue exchange
   __shared__ u32x4 lds[2 * S * RPL * WAVE];
 
   const int lane = threadIdx.x & 63;
@@ -232,56 +233,35 @@ __global__ __launch_bounds__(128) void k_expert_stream(const StreamGemmArgs p) {
   }
   __syncthreads();  // the ring is free from here on
 
-  // -------------------------------------------------------- split-K reduction
-  int* s_last = reinterpret_cast<int*>(lds);
+  // -------------------------------------------------------- split-K partials
+  // With several k-splits each split stores its (scaled) fp32 sums for the
+  // routed rows; a later kernel adds the splits in split order (for gate|up
+  // the split-reduce kernel, which also applies SiLU*up; for down the
+  // combine).  The kernel boundary orders the stores before those reads, so
+  // no device-scope fence or atomic is needed here.
   if (p.ksplit > 1) {
-    const int64_t tile = (int64_t)mb * p.n_tiles + nt;
-    constexpr int64_t PFW = (int64_t)2 * CPL * 4 * WAVE;  // floats per wave partial
-    float* part = p.partial + tile * p.ksplit * 2 * PFW;
-    float* mine = part + ((int64_t)split * 2 + slab) * PFW;
-    if (active) {
+    if (!active) return;
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-        if (rvalid[q])
+    for (int q = 0; q < 2; ++q) {
+      if (!rvalid[q]) continue;
+      const int64_t prow = p0 + 16 * q + li;
+      // column in the weight's N space (gate|up: [0, 2*d_ff); down: [0, d))
+      const int col = (EPI == EPI_SILU_MUL) ? (slab ? p.up_off : 0) + ocol : ocol;
+      float v[NV];
 #pragma unroll
-          for (int c = 0; c < CPL; ++c)
-            *reinterpret_cast<f32x4*>(mine + ((int64_t)(q * CPL + c) * WAVE + lane) * 4) = acc[q][c];
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      *s_last = atomicAdd(p.counters + tile, 1);
-      __threadfence();
-    }
-    __syncthreads();
-    if (*s_last != p.ksplit - 1) return;  // uniform over the workgroup
-    __threadfence();
-    if (active) {
-      f32x4 sum[2][CPL];
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+        for (int c = 0; c < CPL; ++c) v[r * CPL + c] = acc[q][c][r];
+      if (WT == W_FP8) {
+        const float* sc = p.scale + (int64_t)e * p.scale_estride + col;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) sum[q][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int sp = 0; sp < p.ksplit; ++sp) {
-        const float* src = part + ((int64_t)sp * 2 + slab) * PFW;
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-          if (rvalid[q])
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-              const f32x4 v = (sp == split) ? acc[q][c]
-                                            : *reinterpret_cast<const f32x4*>(
-                                                  src + ((int64_t)(q * CPL + c) * WAVE + lane) * 4);
-              sum[q][c] += v;
-            }
+        for (int j = 0; j < NV; ++j) v[j] *= sc[j];
       }
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[q][c] = sum[q][c];
+      char* dst = reinterpret_cast<char*>(p.partial) +
+                  ((int64_t)split * p.partial_split_stride + prow * p.partial_ld + col) * 4;
+      store_act<ACT_F32>(dst, v, NV);
     }
-    if (threadIdx.x == 0) p.counters[tile] = 0;
-    __syncthreads();  // s_last read by all before the exchange reuses the memory
+    return;
   }
 
   // -------------------------------------------------------- epilogue
@@ -343,6 +323,54 @@ __global__ __launch_bounds__(128) void k_expert_stream(const StreamGemmArgs p) {
   }
 }
 
+// h[p, n] = SiLU(sum_s g_s[p, n]) * sum_s u_s[p, n] for the routed rows p,
+// splits added in order.  One workgroup per (row, 2048-column chunk).
+template <int ACT>
+__global__ __launch_bounds__(256) void k_splitk_silu(const float* __restrict__ part, int nsplit,
+                                                     int64_t split_stride, int64_t part_ld,
+                                                     const int32_t* __restrict__ sorted_ids,
+                                                     int d_ff, char* __restrict__ h) {
+  constexpr int ASZ = ACT == ACT_BF16 ? 2 : 4;
+  const int64_t p = blockIdx.x;
+  if (sorted_ids[p] < 0) return;
+  const int n0 = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (n0 >= d_ff) return;
+  float g[8], u[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) g[j] = u[j] = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* row = part + s * split_stride + p * part_ld;
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      const u32x4 a = ld16(row + n0 + 4 * hlf);
+      const u32x4 b = ld16(row + d_ff + n0 + 4 * hlf);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        g[4 * hlf + j] += __uint_as_float(a[j]);
+        u[4 * hlf + j] += __uint_as_float(b[j]);
+      }
+    }
+  }
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = silu(g[j]) * u[j];
+  store_act<ACT>(h + (p * d_ff + n0) * ASZ, v, 8);
+}
+
+hipError_t launch_splitk_silu(int act, const float* part, int nsplit, int64_t split_stride,
+                              int64_t part_ld, const int32_t* sorted_ids, int64_t rows, int d_ff,
+                              void* h, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)rows, (unsigned)((d_ff + 2047) / 2048));
+  if (act == ACT_BF16)
+    hipLaunchKernelGGL(k_splitk_silu<ACT_BF16>, grid, dim3(256), 0, st, part, nsplit, split_stride,
+                       part_ld, sorted_ids, d_ff, reinterpret_cast<char*>(h));
+  else
+    hipLaunchKernelGGL(k_splitk_silu<ACT_F32>, grid, dim3(256), 0, st, part, nsplit, split_stride,
+                       part_ld, sorted_ids, d_ff, reinterpret_cast<char*>(h));
+  return hipGetLastError();
+}
+
 int stream_tile_cols(int w_dtype, int epi) {
   const int sw = 16 * (w_dtype == W_F32 ? DTr<W_F32>::CPL
                                          : (w_dtype == W_FP8 ? DTr<W_FP8>::CPL : DTr<W_BF16>::CPL));
@@ -351,12 +379,6 @@ int stream_tile_cols(int w_dtype, int epi) {
 
 int stream_kstep(int w_dtype) {
   return (w_dtype == W_F32) ? DTr<W_F32>::KSTEP : DTr<W_BF16>::KSTEP;
-}
-
-int64_t stream_partial_floats_per_tile_split(int w_dtype) {
-  const int cpl = w_dtype == W_F32 ? DTr<W_F32>::CPL
-                                   : (w_dtype == W_FP8 ? DTr<W_FP8>::CPL : DTr<W_BF16>::CPL);
-  return (int64_t)2 * 2 * cpl * 4 * WAVE;
 }
 
 template <int ACT, int WT, int EPI>

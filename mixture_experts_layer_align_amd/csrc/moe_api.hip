@@ -11,8 +11,15 @@ using namespace moe;
 namespace {
 
 constexpr int64_t WS_ALIGN = 256;
-constexpr int TARGET_WGS = 512;      // two-wave workgroups resident at once (2 per CU)
+constexpr int ROUTER_TARGET_WGS = 512;
 constexpr int ROUTER_MAX_SPLIT = 16;
+// Expert GEMMs split K only when the blocks x n-tiles work items leave the chip
+// under-filled (fewer than SPLIT_BELOW two-wave workgroups); a split then aims
+// at SPLIT_TARGET workgroups and keeps at least MIN_SPLIT_STEPS k-steps each
+// so the 4-stage load ring still streams.
+constexpr int SPLIT_BELOW = 192;
+constexpr int SPLIT_TARGET = 384;
+constexpr int MIN_SPLIT_STEPS = 8;
 constexpr int64_t MAX_ENTRIES = int64_t(1) << 24;
 
 int64_t up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -49,15 +56,16 @@ int check_ws(void* ws, size_t* ws_bytes, int64_t need, bool* query) {
   return MOE_OK;
 }
 
-// Split K so that items * split workgroups approach TARGET_WGS, keeping at
-// least two k-steps per split and at most max_split splits.  Returns the
-// k-chunk (a multiple of kstep).
-int choose_kchunk(int64_t items, int K, int kstep, int* nsplit, int max_split = 1 << 20) {
+// Number of k-splits: 1 when `items` workgroups reach `below`, else enough to
+// approach `target`, with at least `min_steps` k-steps per split and at most
+// max_split splits.  Returns the k-chunk (a multiple of kstep).
+int choose_kchunk(int64_t items, int K, int kstep, int* nsplit, int below, int target,
+                  int min_steps, int max_split) {
   const int steps = K / kstep;
   items = std::max<int64_t>(items, 1);
   int s = 1;
-  if (items < TARGET_WGS)
-    s = (int)std::min<int64_t>({(TARGET_WGS + items - 1) / items, (int64_t)steps / 2,
+  if (items < below)
+    s = (int)std::min<int64_t>({(target + items - 1) / items, (int64_t)steps / min_steps,
                                 (int64_t)max_split});
   s = std::max(s, 1);
   const int chunk_steps = (steps + s - 1) / s;
@@ -89,7 +97,7 @@ RouterPlan plan_router(const void* x, const void* w_router, int T, int d, int E,
   const int tc = router_tile_cols(act);
   g.n_tiles = (E + tc - 1) / tc;
   g.kchunk = choose_kchunk((int64_t)g.num_mblocks * g.n_tiles, d, router_kstep(act), &g.ksplit,
-                           ROUTER_MAX_SPLIT);
+                           ROUTER_TARGET_WGS, ROUTER_TARGET_WGS, 2, ROUTER_MAX_SPLIT);
   g.out_ld = E;
   g.out_split_stride = (int64_t)T * E;
   r.nsplit = g.ksplit;
@@ -98,8 +106,8 @@ RouterPlan plan_router(const void* x, const void* w_router, int T, int d, int E,
 }
 
 hipError_t run_router(RouterPlan& r, int act, float* partial, const float* bias, int T, int E,
-                      int k, float* logits, int32_t* ids, float* w, int32_t* zero_ptr,
-                      int64_t zero_n, hipStream_t st, moe_trace* tr, int* kidx);
+                      int k, float* logits, int32_t* ids, float* w, hipStream_t st, moe_trace* tr,
+                      int* kidx);
 
 // ------------------------------------------------------------ tracing
 void trace_mark(moe_trace* tr, int* kidx, const char* name, hipStream_t st) {
@@ -111,15 +119,14 @@ void trace_mark(moe_trace* tr, int* kidx, const char* name, hipStream_t st) {
 }
 
 hipError_t run_router(RouterPlan& r, int act, float* partial, const float* bias, int T, int E,
-                      int k, float* logits, int32_t* ids, float* w, int32_t* zero_ptr,
-                      int64_t zero_n, hipStream_t st, moe_trace* tr, int* kidx) {
+                      int k, float* logits, int32_t* ids, float* w, hipStream_t st, moe_trace* tr,
+                      int* kidx) {
   r.g.out = partial;
   trace_mark(tr, kidx, "router_gemm", st);
   hipError_t e = launch_router_gemm(act, r.g, st);
   if (e != hipSuccess) return e;
   trace_mark(tr, kidx, "topk", st);
-  return launch_topk(partial, r.nsplit, (int64_t)T * E, bias, T, E, k, logits, ids, w, zero_ptr,
-                     zero_n, st);
+  return launch_topk(partial, r.nsplit, (int64_t)T * E, bias, T, E, k, logits, ids, w, st);
 }
 
 // Shapes and dtypes; data pointers are checked only when work is enqueued
@@ -173,7 +180,7 @@ int moe_route(const void* x, const void* w_router, const float* logit_bias, int 
     return MOE_ERR_INVALID;
   int kidx = 0;
   hipError_t e = run_router(r, act, partial, logit_bias, T, E, k, logits, topk_ids, topk_w,
-                            nullptr, 0, static_cast<hipStream_t>(stream), nullptr, &kidx);
+                            static_cast<hipStream_t>(stream), nullptr, &kidx);
   return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
@@ -248,13 +255,10 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   const int64_t est_blocks =
       std::min<int64_t>(nblocks, std::max<int64_t>(std::min<int64_t>(E, n), (n + bm - 1) / bm));
   int gu_split, dn_split;
-  const int gu_chunk = choose_kchunk(std::max<int64_t>(est_blocks, 1) * gu_tiles, d, kstep, &gu_split);
-  const int dn_chunk = choose_kchunk(std::max<int64_t>(est_blocks, 1) * dn_tiles, dff, kstep, &dn_split);
-  const int64_t pf = stream_partial_floats_per_tile_split(wdt);
-  const int64_t gu_partial = gu_split > 1 ? nblocks * gu_tiles * gu_split * pf : 0;
-  const int64_t dn_partial = dn_split > 1 ? nblocks * dn_tiles * dn_split * pf : 0;
-  const int64_t ncounters = nblocks * std::max(gu_tiles, dn_tiles);
-
+  const int gu_chunk = choose_kchunk(std::max<int64_t>(est_blocks, 1) * gu_tiles, d, kstep,
+                                     &gu_split, SPLIT_BELOW, SPLIT_TARGET, MIN_SPLIT_STEPS, 64);
+  const int dn_chunk = choose_kchunk(std::max<int64_t>(est_blocks, 1) * dn_tiles, dff, kstep,
+                                     &dn_split, SPLIT_BELOW, SPLIT_TARGET, MIN_SPLIT_STEPS, 64);
   Carve c(workspace);
   float* r_partial = c.take<float>(std::max<int64_t>(r.partial_floats, 1));
   int32_t* ids = c.take<int32_t>(std::max<int64_t>(n, 1));
@@ -266,9 +270,9 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   int32_t* bexp = c.take<int32_t>(std::max<int64_t>(nblocks, 1));
   char* al_ws = c.take<char>(std::max<int64_t>(align_workspace_bytes((int)n, E), 1));
   char* h = c.take<char>(std::max<int64_t>(cap * dff * ab, 1));
-  float* y = c.take<float>(std::max<int64_t>(cap * d, 1));
-  float* gpart = c.take<float>(std::max<int64_t>(std::max(gu_partial, dn_partial), 1));
-  int32_t* counters = c.take<int32_t>(std::max<int64_t>(ncounters, 1));
+  // per-slot expert outputs (fp32), or their k-split partial sums
+  float* y = c.take<float>(std::max<int64_t>(dn_split * cap * d, 1));
+  float* gu_part = gu_split > 1 ? c.take<float>(gu_split * cap * 2 * dff) : nullptr;
   bool query;
   rc = check_ws(workspace, workspace_bytes, c.off, &query);
   if (rc != MOE_OK || query) return rc;
@@ -292,8 +296,8 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   hipStream_t st = static_cast<hipStream_t>(stream);
   int kidx = 0;
 
-  hipError_t e = run_router(r, act, r_partial, L->logit_bias, T, E, k, logits, ids, tw, counters,
-                            ncounters, st, tr, &kidx);
+  hipError_t e = run_router(r, act, r_partial, L->logit_bias, T, E, k, logits, ids, tw, st, tr,
+                            &kidx);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
 
   AlignArgs a{};
@@ -332,13 +336,20 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g.n_tiles = gu_tiles;
   g.ksplit = gu_split;
   g.kchunk = gu_chunk;
-  g.partial = gpart;
-  g.counters = counters;
+  g.partial = gu_part;
+  g.partial_ld = 2 * (int64_t)dff;
+  g.partial_split_stride = cap * 2 * dff;
   g.out = h;
   g.out_ld = dff;
   trace_mark(tr, &kidx, "gate_up", st);
   e = launch_stream_gemm(act, wdt, EPI_SILU_MUL, g, st);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
+  if (gu_split > 1) {
+    trace_mark(tr, &kidx, "gate_up_reduce", st);
+    e = launch_splitk_silu(act, gu_part, gu_split, cap * 2 * dff, 2 * (int64_t)dff, sorted, cap,
+                           dff, h, st);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+  }
 
   StreamGemmArgs g2{};
   g2.a = h;
@@ -358,8 +369,9 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g2.n_tiles = dn_tiles;
   g2.ksplit = dn_split;
   g2.kchunk = dn_chunk;
-  g2.partial = gpart;
-  g2.counters = counters;
+  g2.partial = y;
+  g2.partial_ld = d;
+  g2.partial_split_stride = cap * d;
   g2.out = y;
   g2.out_ld = d;
   trace_mark(tr, &kidx, "down", st);
@@ -367,7 +379,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   if (e != hipSuccess) return MOE_ERR_DEVICE;
 
   trace_mark(tr, &kidx, "combine", st);
-  e = launch_combine(act, y, inv, tw, T, k, d, out, st);
+  e = launch_combine(act, y, dn_split, cap * d, inv, tw, T, k, d, out, st);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   trace_mark(tr, &kidx, nullptr, st);
   if (tr != nullptr) tr->n_kernels = kidx - 1;

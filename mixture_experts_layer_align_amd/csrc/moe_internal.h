@@ -46,8 +46,9 @@ struct StreamGemmArgs {
   int n_tiles;
   int ksplit;
   int kchunk;
-  float* partial;         // split-K partial tiles (ksplit > 1)
-  int32_t* counters;      // one per (m-block, n-tile), zero on entry
+  float* partial;         // ksplit > 1: fp32 partial sums [ksplit][rows][partial_ld]
+  int64_t partial_ld;     //   (columns in the weight's N space)
+  int64_t partial_split_stride;
   void* out;
   int64_t out_ld;
   int64_t out_split_stride;  // router: elements between split planes
@@ -60,9 +61,12 @@ constexpr int STREAM_BM = 32;
 int stream_tile_cols(int w_dtype, int epi);
 // K granularity of one k-step.
 int stream_kstep(int w_dtype);
-// Floats of partial storage one (tile, split) needs.
-int64_t stream_partial_floats_per_tile_split(int w_dtype);
 
+// h = SiLU(sum of gate partials) * (sum of up partials), splits in order, for
+// the rows whose slot holds a routed entry.
+hipError_t launch_splitk_silu(int act_dtype, const float* part, int nsplit, int64_t split_stride,
+                              int64_t part_ld, const int32_t* sorted_ids, int64_t rows, int d_ff,
+                              void* h, hipStream_t st);
 hipError_t launch_stream_gemm(int act_dtype, int w_dtype, int epi, const StreamGemmArgs& a,
                               hipStream_t st);
 
@@ -75,11 +79,9 @@ hipError_t launch_router_gemm(int act_dtype, const StreamGemmArgs& a, hipStream_
 // ------------------------------------------------------------ routing
 
 // Sum split-K partial logits, add bias, write logits (optional), select top-k
-// with ties to the lower index and renormalised softmax weights.  Also zeroes
-// `zero_ptr[0..zero_n)` (counters used by later kernels of the same call).
+// with ties to the lower index and renormalised softmax weights.
 hipError_t launch_topk(const float* partial, int nsplit, int64_t split_stride, const float* bias,
-                       int T, int E, int k, float* logits, int32_t* ids, float* w,
-                       int32_t* zero_ptr, int64_t zero_n, hipStream_t st);
+                       int T, int E, int k, float* logits, int32_t* ids, float* w, hipStream_t st);
 
 // ------------------------------------------------------------ alignment
 
@@ -107,8 +109,10 @@ hipError_t launch_align(AlignArgs a, void* ws, hipStream_t st);
 
 // ------------------------------------------------------------ combine
 
-// y: per-slot expert outputs, fp32 [cap, d]
-hipError_t launch_combine(int act_dtype, const float* y, const int32_t* inv_pos, const float* w,
-                          int T, int k, int d, void* out, hipStream_t st);
+// y: per-slot expert outputs, fp32 [nsplit][cap, d] (k-split partial sums,
+// added in split order before the weighting)
+hipError_t launch_combine(int act_dtype, const float* y, int nsplit, int64_t split_stride,
+                          const int32_t* inv_pos, const float* w, int T, int k, int d, void* out,
+                          hipStream_t st);
 
 }  // namespace moe

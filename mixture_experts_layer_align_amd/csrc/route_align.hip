@@ -39,13 +39,9 @@ template <int V>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial, int nsplit,
                                               int64_t split_stride, const float* __restrict__ bias,
                                               int T, int E, int k, float* __restrict__ logits,
-                                              int32_t* __restrict__ ids, float* __restrict__ wout,
-                                              int32_t* __restrict__ zero_ptr, int64_t zero_n) {
+                                              int32_t* __restrict__ ids, float* __restrict__ wout) {
   __shared__ float sel_v[4][MAX_EXPERTS];
   __shared__ int sel_i[4][MAX_EXPERTS];
-  for (int64_t z = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; z < zero_n;
-       z += (int64_t)gridDim.x * blockDim.x)
-    zero_ptr[z] = 0;
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -110,13 +106,12 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial,
 }
 
 hipError_t launch_topk(const float* partial, int nsplit, int64_t split_stride, const float* bias,
-                       int T, int E, int k, float* logits, int32_t* ids, float* w,
-                       int32_t* zero_ptr, int64_t zero_n, hipStream_t st) {
+                       int T, int E, int k, float* logits, int32_t* ids, float* w, hipStream_t st) {
   const int grid = (T + 3) / 4;
   if (grid == 0) return hipSuccess;
 #define MOE_TOPK(V_)                                                                           \
   hipLaunchKernelGGL(k_topk<V_>, dim3(grid), dim3(256), 0, st, partial, nsplit, split_stride, \
-                     bias, T, E, k, logits, ids, w, zero_ptr, zero_n)
+                     bias, T, E, k, logits, ids, w)
   if (E <= 64) MOE_TOPK(1);
   else if (E <= 128) MOE_TOPK(2);
   else if (E <= 256) MOE_TOPK(4);
