@@ -11,8 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["moe_api.hip", "router_gemm.hip", "expert_gemm_stream.hip", "route_align.hip",
-           "combine.hip"]
+SOURCES = ["moe_api.hip", "router_gemm.hip", "expert_gemm_stream.hip", "expert_gemm_tiled.hip",
+           "route_align.hip", "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

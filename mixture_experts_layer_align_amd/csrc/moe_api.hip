@@ -18,6 +18,12 @@ constexpr int ROUTER_MAX_SPLIT = 16;
 // at SPLIT_TARGET workgroups and keeps at least MIN_SPLIT_STEPS k-steps each
 // so the 4-stage load ring still streams.
 constexpr int SPLIT_BELOW = 192;
+// Average routed rows per expert from which the LDS-tiled GEMM (128-row
+// blocks, MFMA-bound) replaces the weight-streaming GEMM (32-row blocks).
+constexpr int TILED_MIN_ROWS = 64;
+// ... and from which it uses 256-row blocks (less LDS traffic per flop, more
+// padding per expert).
+constexpr int TILED_BM256_ROWS = 1024;
 constexpr int SPLIT_TARGET = 384;
 constexpr int MIN_SPLIT_STEPS = 8;
 constexpr int64_t MAX_ENTRIES = int64_t(1) << 24;
@@ -238,8 +244,11 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   const int act = act_code(L->act_dtype);
   const int wdt = w_code(L->w_dtype);
   const int ab = act_bytes(L->act_dtype);
-  const int bm = STREAM_BM;
   const int64_t n = (int64_t)T * k;
+  // regime: thick blocks go to the MFMA-tiled GEMM when its shapes fit
+  const bool tiled = act == ACT_BF16 && wdt == W_BF16 && n >= (int64_t)TILED_MIN_ROWS * E &&
+                     d % TILED_BN == 0 && dff % (TILED_BN / 2) == 0;
+  const int bm = !tiled ? STREAM_BM : (n >= (int64_t)TILED_BM256_ROWS * E ? 256 : 128);
   const int64_t cap = moe_align_capacity(T, E, k, bm);
   const int64_t nblocks = cap / bm;
 
@@ -247,18 +256,20 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
 
   // expert GEMM plans
   const int kstep = stream_kstep(wdt);
-  const int gu_tc = stream_tile_cols(wdt, EPI_SILU_MUL);
-  const int dn_tc = stream_tile_cols(wdt, EPI_STORE);
+  const int gu_tc = tiled ? TILED_BN / 2 : stream_tile_cols(wdt, EPI_SILU_MUL);
+  const int dn_tc = tiled ? TILED_BN : stream_tile_cols(wdt, EPI_STORE);
   const int gu_tiles = dff / gu_tc;
   const int dn_tiles = (d + dn_tc - 1) / dn_tc;
   // blocks expected to carry rows: one per active expert plus the overflow
   const int64_t est_blocks =
       std::min<int64_t>(nblocks, std::max<int64_t>(std::min<int64_t>(E, n), (n + bm - 1) / bm));
-  int gu_split, dn_split;
-  const int gu_chunk = choose_kchunk(std::max<int64_t>(est_blocks, 1) * gu_tiles, d, kstep,
-                                     &gu_split, SPLIT_BELOW, SPLIT_TARGET, MIN_SPLIT_STEPS, 64);
-  const int dn_chunk = choose_kchunk(std::max<int64_t>(est_blocks, 1) * dn_tiles, dff, kstep,
-                                     &dn_split, SPLIT_BELOW, SPLIT_TARGET, MIN_SPLIT_STEPS, 64);
+  int gu_split = 1, dn_split = 1, gu_chunk = d, dn_chunk = dff;
+  if (!tiled) {
+    gu_chunk = choose_kchunk(std::max<int64_t>(est_blocks, 1) * gu_tiles, d, kstep, &gu_split,
+                             SPLIT_BELOW, SPLIT_TARGET, MIN_SPLIT_STEPS, 64);
+    dn_chunk = choose_kchunk(std::max<int64_t>(est_blocks, 1) * dn_tiles, dff, kstep, &dn_split,
+                             SPLIT_BELOW, SPLIT_TARGET, MIN_SPLIT_STEPS, 64);
+  }
   Carve c(workspace);
   float* r_partial = c.take<float>(std::max<int64_t>(r.partial_floats, 1));
   int32_t* ids = c.take<int32_t>(std::max<int64_t>(n, 1));
@@ -342,7 +353,8 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g.out = h;
   g.out_ld = dff;
   trace_mark(tr, &kidx, "gate_up", st);
-  e = launch_stream_gemm(act, wdt, EPI_SILU_MUL, g, st);
+  e = tiled ? launch_tiled_gemm(EPI_SILU_MUL, bm, g, st)
+            : launch_stream_gemm(act, wdt, EPI_SILU_MUL, g, st);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   if (gu_split > 1) {
     trace_mark(tr, &kidx, "gate_up_reduce", st);
@@ -375,7 +387,8 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g2.out = y;
   g2.out_ld = d;
   trace_mark(tr, &kidx, "down", st);
-  e = launch_stream_gemm(act, wdt, EPI_STORE, g2, st);
+  e = tiled ? launch_tiled_gemm(EPI_STORE, bm, g2, st)
+            : launch_stream_gemm(act, wdt, EPI_STORE, g2, st);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
 
   trace_mark(tr, &kidx, "combine", st);

@@ -72,6 +72,11 @@ SMALL = [
     (8, 2, 256, 256, "bf16", "fp8", 257, 1.2),
     (4, 2, 128, 128, "f32", "f32", 300, 0.5),
     (8, 2, 128, 128, "bf16", "bf16", 0, None),       # empty batch
+    # >= 64 routed rows per expert and d % 256 == 0: the MFMA-tiled GEMM
+    (4, 2, 256, 256, "bf16", "bf16", 300, None),
+    (8, 2, 512, 384, "bf16", "bf16", 700, 1.2),      # skewed, ragged blocks
+    (1, 1, 256, 128, "bf16", "bf16", 200, None),     # one expert, 2 blocks
+    (16, 4, 768, 640, "bf16", "bf16", 1111, 0.8),
 ]
 
 
@@ -85,18 +90,21 @@ def test_forward_small_layers(E, k, d, d_ff, act, wdt, T, zipf):
     run_and_check(layer, x, what="small")
 
 
-def test_forward_all_tokens_on_one_expert_in_full_blocks():
-    # a one-hot bias sends every token's slot 0 to expert 3; 64 tokens fill
-    # exactly two 32-row blocks
+@pytest.mark.parametrize("T", [64, 1024])
+def test_forward_all_tokens_on_one_expert_in_full_blocks(T):
+    # a one-hot bias sends every token's slot 0 to expert 3; the tokens fill
+    # whole blocks (two 32-row blocks of the streaming GEMM at T=64, eight
+    # 128-row blocks of the tiled GEMM at T=1024)
     sh = LayerShape(250, "onehot", E=8, k=1, d=256, d_ff=128, act="bf16", wdt="bf16", seed=9)
-    layer = make_layer(sh, 64, "cuda", zipf=None)
+    layer = make_layer(sh, T, "cuda", zipf=None)
     bias = torch.zeros(8, dtype=torch.float32, device="cuda")
     bias[3] = 1e4
     layer = dataclasses.replace(layer, bias=bias)
-    x = make_tokens(sh, 64, "cuda")
+    x = make_tokens(sh, T, "cuda")
     _, rb, bm = run_and_check(layer, x, what="one-hot")
     c = rb["counts"].cpu().numpy()
-    assert c[3] == 64 and c.sum() == 64 and 64 % bm == 0
+    assert c[3] == T and c.sum() == T and T % bm == 0
+    assert bm == (128 if T == 1024 else 32)
 
 
 def test_forward_is_deterministic():
