@@ -11,26 +11,31 @@
 //     before the single store of h ("La fusion de noyaux", section 4.2, GEMM +
 //     epilogue; the concatenated d x 2*d_ff gate|up); each wave owns a
 //     (BM/2) x 128 sub-tile;
-//   * K advances 64 at a time through an LDS pipeline (2 or 3 stages) filled by
-//     direct loads (global_load_lds_dwordx4): the token tile is gathered row
-//     by row from x by slot (the permuted activations are never
-//     materialised), the weight tile is copied untransposed ([K, N], N
-//     contiguous, the B[K,N] of the vLLM post's A[M,K] x B[K,N]);
-//   * within a stage the two 32-deep k-steps' fragments are read into two
-//     register sets, so the second step's LDS reads run under the first
-//     step's MFMAs (reads and waits are counted explicitly);
+//   * K advances 32 at a time (one v_mfma_f32_16x16x32_bf16 deep) through a
+//     ring of LDS stages (4 for BM = 256, 6 for BM = 128) filled by direct
+//     loads (global_load_lds_dwordx4): the token tile is gathered row by row
+//     from x by slot (the permuted activations are never materialised), the
+//     weight tile is copied untransposed ([K, N], N contiguous, the B[K,N] of
+//     the vLLM post's A[M,K] x B[K,N]);
+//   * the loop is software-pipelined per k-step: while the MFMAs of step j
+//     run on fragments already in registers, the same instruction stream
+//     reads step j+1's fragments from LDS and issues the direct loads that
+//     refill the stage step j-1 used, spread between the MFMAs (and pinned
+//     there), so the LDS, the vector memory path and the matrix cores are
+//     busy at once; one workgroup barrier per step publishes the stage that
+//     landed and frees the one just consumed;
 //   * the weight operand's K-contiguous MFMA fragments come from gfx950's
 //     transposing LDS read (ds_read_b64_tr_b16: within each 16-lane group,
 //     lane i receives element i%4 of the 8-byte pieces addressed by lanes
 //     4v + i/4, v = 0..3 — so lanes that address 4 consecutive rows x 16
-//     columns hand lane i column i of those rows), two per
-//     v_mfma_f32_16x16x32_bf16 fragment;
+//     columns hand lane i column i of those rows), two per fragment;
 //   * both LDS tiles are XOR-swizzled per row so the fragment reads hit
 //     distinct banks;
 //   * consecutive workgroups walk 8 row blocks before the next weight tile,
 //     so a weight tile is fetched from HBM once for up to 8 row blocks and a
 //     token block stays resident in its XCD's L2 across its weight tiles.
 #include <type_traits>
+#include <utility>
 
 #include "moe_common.h"
 #include "moe_internal.h"
@@ -40,28 +45,35 @@ namespace moe {
 namespace {
 
 constexpr int TBN = 256;  // weight columns per tile
-constexpr int TBK = 64;   // k per pipeline stage
+constexpr int TBK = 32;   // k per step and per LDS stage
 constexpr int GROUP_M = 8;
-constexpr int B_STAGE_BYTES = TBK * TBN * 2;            // 32 KB
-constexpr int B_DMA_PER_THREAD = TBK * (TBN / 8) / 256;  // 8
+constexpr int B_STAGE_BYTES = TBK * TBN * 2;            // 16 KB
+constexpr int B_DPT = TBK * (TBN / 8) / 256;            // direct loads per thread: 4
 
 template <int BM>
 struct TCfg {
-  static constexpr int STAGES = BM == 256 ? 2 : 3;
+  static constexpr int STAGES = BM == 256 ? 4 : 6;
   static constexpr int A_STAGE_BYTES = BM * TBK * 2;
   static constexpr int STAGE_BYTES = A_STAGE_BYTES + B_STAGE_BYTES;
-  static constexpr int A_DMA_PER_THREAD = BM * (TBK / 8) / 256;
-  static constexpr int DMA_PER_STAGE = A_DMA_PER_THREAD + B_DMA_PER_THREAD;
+  static constexpr int A_DPT = BM * (TBK / 8) / 256;   // direct loads per thread
+  static constexpr int DPT = A_DPT + B_DPT;
   static constexpr int MI = BM / 32;                   // 16-row fragments per wave
-  static constexpr int READS_PER_KSTEP = MI + 16;      // LDS reads per wave per k-step
+  static constexpr int NMFMA = MI * 8;                 // MFMAs per wave per step
+  static constexpr int NREAD = MI + 16;                // LDS reads per wave per step
+  static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
 };
 
 constexpr int vmcnt_imm(int n) {
   return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14);
 }
 
-// swizzles: chunk position of logical 16-byte chunk c in row r
-__device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// swizzles: LDS chunk position of logical 16-byte chunk c in row r.
+//   A rows are 4 chunks (32 k x bf16): the 16 rows of a fragment read land in
+//   16 distinct 16-byte bank groups, and any 8 consecutive rows in 8.
+//   B rows are 32 chunks (256 columns).
+__device__ __forceinline__ int swz_a(int r) {
+  return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
+}
 __device__ __forceinline__ int swz_b(int r) { return 2 * ((r & 3) | ((r >> 1) & 4)); }
 
 __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
@@ -93,28 +105,57 @@ __device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
   return v;
 }
 
+// The k-loop MFMAs are inline assembly on accumulators pinned to AGPRs
+// ("+a"): with builtins the register allocator moves accumulators between
+// AGPRs and VGPRs at every loop back-edge once fragments are carried across
+// it.  The compiler does not see these as MFMAs, so the code around them
+// keeps the hazards away by construction: the accumulators are first written
+// by an MFMA with an inline-constant zero C operand (no VALU write precedes
+// an MFMA read of them), nothing but these MFMAs touches them inside the
+// loop, and s_nop padding separates the last MFMA from the epilogue's reads.
+__device__ __forceinline__ void mfma_acc(f32x4& acc, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_zero(f32x4& acc, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+}
+
 template <int MI>
 struct Frags {
   u32x4 a[MI];
   u32x2 bl[8], bh[8];
 };
 
-// s_waitcnt lgkmcnt(N) with the fragment registers tied to it, so nothing
+// s_waitcnt lgkmcnt(0) with the fragment registers tied to it, so nothing
 // that reads them can be scheduled before the wait
-template <int N, int MI>
+template <int MI>
 __device__ __forceinline__ void wait_frags(Frags<MI>& f) {
-  static_assert(N >= 0 && N <= 15, "lgkmcnt field");
 #pragma unroll
   for (int i = 0; i < MI; ++i) asm volatile("" : "+v"(f.a[i]));
-  asm volatile("s_waitcnt lgkmcnt(%16)"
+  asm volatile("s_waitcnt lgkmcnt(0)"
                : "+v"(f.bl[0]), "+v"(f.bl[1]), "+v"(f.bl[2]), "+v"(f.bl[3]), "+v"(f.bl[4]),
                  "+v"(f.bl[5]), "+v"(f.bl[6]), "+v"(f.bl[7]), "+v"(f.bh[0]), "+v"(f.bh[1]),
                  "+v"(f.bh[2]), "+v"(f.bh[3]), "+v"(f.bh[4]), "+v"(f.bh[5]), "+v"(f.bh[6]),
-                 "+v"(f.bh[7])
-               : "n"(N));
+                 "+v"(f.bh[7]));
 #pragma unroll
   for (int i = 0; i < MI; ++i) asm volatile("" : "+v"(f.a[i]));
 }
+
+template <int I>
+using IC = std::integral_constant<int, I>;
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(IC<Is>{}), ...);
+}
+// f(IC<0>{}), ..., f(IC<N-1>{}) in order
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Position of op i of n spread over the first `span` of `slots` MFMAs:
+// op i goes right after MFMA (i * span) / n.
+constexpr int slot_of(int i, int n, int span) { return (i * span) / n; }
 
 }  // namespace
 
@@ -142,63 +183,61 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
   if (e < 0) return;
   const int p0 = mb * BM;
 
-  // ---------------------------------------------------- DMA source addresses
-  // A: slot s = (wave*A_DMA + i)*64 + lane -> row s/8, position s%8; the
-  // lane's row index (token, or h row) is kept, the chunk is recomputed
-  int a_row[C::A_DMA_PER_THREAD];
+  // ---------------------------------------------------- direct-load sources
+  // A slot s = (wave*A_DPT + i)*64 + lane -> tile row s/4, position s%4 =
+  // lane%4 (64-slot blocks start at multiples of 4 rows)
+  const char* a_src[C::A_DPT];
 #pragma unroll
-  for (int i = 0; i < C::A_DMA_PER_THREAD; ++i) {
-    const int r = ((wave * C::A_DMA_PER_THREAD + i) * 64 + lane) >> 3;
+  for (int i = 0; i < C::A_DPT; ++i) {
+    const int r = ((wave * C::A_DPT + i) * 64 + lane) >> 2;
     const int sid = p.sorted_ids[p0 + r];
     int row = 0;  // padding rows read row 0; their results are never stored
     if (sid >= 0) row = (p.a_mode == A_GATHER) ? sid / p.topk : p0 + r;
-    a_row[i] = row;
+    const int c = (lane & 3) ^ swz_a(r);
+    a_src[i] = reinterpret_cast<const char*>(p.a) + ((int64_t)row * p.a_ld + 8 * c) * 2;
   }
-  // A rows are 8 chunks, so slot s's row is s/8 and its chunk position s%8 =
-  // lane%8 for every i (the 64-lane blocks start at multiples of 8 rows)
-  const int a_pos = lane & 7;
-  const char* xa = reinterpret_cast<const char*>(p.a);
-  const char* wexp = reinterpret_cast<const char*>(p.w) + (int64_t)e * p.w_estride * 2;
+  // B slot s = (wave*B_DPT + i)*64 + lane -> k row s/32, position s%32
+  const char* b_src[B_DPT];
+#pragma unroll
+  for (int i = 0; i < B_DPT; ++i) {
+    const int r = (wave * B_DPT + i) * 2 + (lane >> 5);
+    const int c = (lane & 31) ^ swz_b(r);
+    int col;
+    if constexpr (EPI == EPI_SILU_MUL)
+      col = (c < 16) ? nt * 128 + 8 * c : p.up_off + nt * 128 + 8 * (c - 16);
+    else
+      col = nt * TBN + 8 * c;
+    b_src[i] = reinterpret_cast<const char*>(p.w) +
+               ((int64_t)e * p.w_estride + (int64_t)r * p.w_ld + col) * 2;
+  }
+  const int64_t b_kstep = (int64_t)TBK * p.w_ld * 2;  // bytes per k-step of B
   const int nk = p.K / TBK;
 
-  auto issue = [&](int stage, int kt) __attribute__((always_inline)) {
-    char* sa = lds + stage * C::STAGE_BYTES;
-    char* sb = sa + C::A_STAGE_BYTES;
-    const int64_t k0 = (int64_t)kt * TBK;
-#pragma unroll
-    for (int i = 0; i < C::A_DMA_PER_THREAD; ++i) {
-      const int r = ((wave * C::A_DMA_PER_THREAD + i) * 64 + lane) >> 3;
-      const int c = a_pos ^ swz_a(r);
-      dma16(xa + ((int64_t)a_row[i] * p.a_ld + k0 + 8 * c) * 2,
-            sa + (wave * C::A_DMA_PER_THREAD + i) * 1024);
+  // the d-th direct load (of DPT) of k-step kt into stage st
+  auto dma = [&](auto d_c, int st, int kt) __attribute__((always_inline)) {
+    constexpr int d = decltype(d_c)::value;
+    char* sa = lds + st * C::STAGE_BYTES;
+    if constexpr (d < C::A_DPT) {
+      dma16(a_src[d] + (int64_t)kt * (TBK * 2), sa + (wave * C::A_DPT + d) * 1024);
+    } else {
+      constexpr int i = d - C::A_DPT;
+      dma16(b_src[i] + kt * b_kstep, sa + C::A_STAGE_BYTES + (wave * B_DPT + i) * 1024);
     }
-#pragma unroll
-    for (int i = 0; i < B_DMA_PER_THREAD; ++i) {
-      // B slot s = (wave*8 + i)*64 + lane -> row s/32, position s%32
-      const int r = (wave * B_DMA_PER_THREAD + i) * 2 + (lane >> 5);
-      const int c = (lane & 31) ^ swz_b(r);
-      int col;
-      if constexpr (EPI == EPI_SILU_MUL)
-        col = (c < 16) ? nt * 128 + 8 * c : p.up_off + nt * 128 + 8 * (c - 16);
-      else
-        col = nt * TBN + 8 * c;
-      dma16(wexp + ((k0 + r) * p.w_ld + col) * 2, sb + (wave * B_DMA_PER_THREAD + i) * 1024);
-    }
+  };
+  auto dma_all = [&](int st, int kt) __attribute__((always_inline)) {
+    static_for<C::DPT>([&](auto d) __attribute__((always_inline)) { dma(d, st, kt); });
   };
 
   // ---------------------------------------------------- fragment addresses
-  // A fragment mi, k-step ks: row R = wm*BM/2 + mi*16 + lane%16, chunk
-  // ks*4 + lane/16.  R%16 = lane%16, so the swizzle is the lane's own and the
-  // address is a per-lane base (one per ks) plus the immediate mi*2048.
+  // A fragment mi: row R = wm*BM/2 + mi*16 + lane%16, chunk lane/16.
+  // R%16 = lane%16, so the swizzle is the lane's own and the address is a
+  // per-lane base plus the immediate mi*1024.
   const int lm = lane & 15, lg = lane >> 4;
   const uint32_t lds_base = lds_off(lds);
-  uint32_t a_base[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-    a_base[ks] = (uint32_t)(((wm * (BM / 2) + lm) * 8 + ((ks * 4 + lg) ^ swz_a(lm))) * 16);
-  // B fragment ni, k-step ks, half h: row kr = ks*32 + 8*lg + lm/4 + 4h,
-  // chunk c0(ni) + (lm%4)/2, 8-byte half lm&1.  swz_b(kr) depends only on
-  // lm/4 and lg&1, so it is the lane's own; ks and h are immediates.
+  const uint32_t a_base = (uint32_t)(((wm * (BM / 2) + lm) * 4 + (lg ^ swz_a(lm))) * 16);
+  // B fragment ni, half h: k row 8*lg + lm/4 + 4h, chunk c0(ni) + (lm%4)/2,
+  // 8-byte half lm&1.  swz_b of that row depends only on lm/4 and lg&1, so
+  // it is the lane's own; h is an immediate.
   const int xb = swz_b(8 * lg + (lm >> 2));
   uint32_t b_base[8];
 #pragma unroll
@@ -209,75 +248,95 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
     else
       c0 = 2 * (wn * 8 + ni);
     const int row = 8 * lg + (lm >> 2);
-    b_base[ni] = (uint32_t)((row * 32 + ((c0 ^ xb) + ((lm & 3) >> 1))) * 16 + (lm & 1) * 8);
+    b_base[ni] = (uint32_t)((row * 32 + ((c0 ^ xb) + ((lm & 3) >> 1))) * 16 + (lm & 1) * 8) +
+                 C::A_STAGE_BYTES;
   }
 
-  auto read_frags = [&](Frags<MI>& f, uint32_t sa, uint32_t sb, auto ks_c)
-                        __attribute__((always_inline)) {
-    constexpr int ks = decltype(ks_c)::value;
-    const uint32_t ab = sa + a_base[ks];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      // unrolled: mi is a compile-time constant, so is the offset
-      switch (mi) {
-        case 0: f.a[0] = lds_read_b128<0>(ab); break;
-        case 1: f.a[1] = lds_read_b128<2048>(ab); break;
-        case 2: f.a[2] = lds_read_b128<4096>(ab); break;
-        case 3: f.a[3] = lds_read_b128<6144>(ab); break;
-        case 4: f.a[4 % MI] = lds_read_b128<8192>(ab); break;
-        case 5: f.a[5 % MI] = lds_read_b128<10240>(ab); break;
-        case 6: f.a[6 % MI] = lds_read_b128<12288>(ab); break;
-        case 7: f.a[7 % MI] = lds_read_b128<14336>(ab); break;
-      }
-    }
-#pragma unroll
-    for (int ni = 0; ni < 8; ++ni) {
-      const uint32_t bb = sb + b_base[ni];
-      f.bl[ni] = lds_read_tr16<ks * 32 * 512>(bb);
-      f.bh[ni] = lds_read_tr16<ks * 32 * 512 + 4 * 512>(bb);
+  // r-th fragment read (of NREAD) of the stage at LDS offset st_off into f
+  auto read = [&](auto r_c, Frags<MI>& f, uint32_t st_off) __attribute__((always_inline)) {
+    constexpr int r = decltype(r_c)::value;
+    if constexpr (r < MI) {
+      f.a[r] = lds_read_b128<r * 1024>(st_off + a_base);
+    } else {
+      constexpr int ni = (r - MI) >> 1;
+      if constexpr (((r - MI) & 1) == 0)
+        f.bl[ni] = lds_read_tr16<0>(st_off + b_base[ni]);
+      else
+        f.bh[ni] = lds_read_tr16<4 * 512>(st_off + b_base[ni]);
     }
   };
 
   f32x4 acc[MI][8];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto mfmas = [&](const Frags<MI>& f) __attribute__((always_inline)) {
-#pragma unroll
-    for (int ni = 0; ni < 8; ++ni) {
-      const u32x4 bf = {f.bl[ni][0], f.bl[ni][1], f.bh[ni][0], f.bh[ni][1]};
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) acc[mi][ni] = mfma_bf16_16x16x32(f.a[mi], bf, acc[mi][ni]);
-    }
+  // One k-step: MFMAs on `cur`; between them, the reads of `nxt` from the
+  // stage at nxt_off (within the first 3/4 of the MFMAs, so they land before
+  // the step ends) and the direct loads of k-step refill_kt into stage
+  // refill_st.  Every op is pinned where it stands.  FIRST: the accumulators
+  // start from zero.
+  auto step = [&](auto first_c, Frags<MI>& cur, Frags<MI>& nxt, uint32_t nxt_off, int refill_st,
+                  int refill_kt) __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first_c)::value;
+    constexpr int NM = C::NMFMA;
+    static_for<NM>([&](auto i_c) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_c)::value;
+      constexpr int ni = i / MI, mi = i % MI;
+      const u32x4 bf = {cur.bl[ni][0], cur.bl[ni][1], cur.bh[ni][0], cur.bh[ni][1]};
+      if constexpr (FIRST)
+        mfma_zero(acc[mi][ni], cur.a[mi], bf);
+      else
+        mfma_acc(acc[mi][ni], cur.a[mi], bf);
+      static_for<C::NREAD>([&](auto r_c) __attribute__((always_inline)) {
+        if constexpr (slot_of(decltype(r_c)::value, C::NREAD, (3 * NM) / 4) == i)
+          read(r_c, nxt, nxt_off);
+      });
+      static_for<C::DPT>([&](auto d_c) __attribute__((always_inline)) {
+        if constexpr (slot_of(decltype(d_c)::value, C::DPT, NM) == i)
+          dma(d_c, refill_st, refill_kt);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   // ---------------------------------------------------- main loop
+  // The stage of k-step kt is kt % S.  At step kt, k-step kt+1 has landed
+  // (waited for before the barrier) and every wave has finished reading stage
+  // kt%S (fragments kt were read and waited for in step kt-1), so that stage
+  // is refilled with k-step kt+S during the MFMAs while fragments kt+1 are
+  // read.  Every step has the same shape: past the end of K the refill
+  // reloads k-step kt (in bounds, never read again) and the last step's
+  // reads of the following stage are discarded, so S-1 k-steps of loads are
+  // always in flight.
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < nk) issue(s, s);
+  for (int s = 0; s < S; ++s) dma_all(s, s < nk ? s : 0);
   Frags<MI> f0, f1;
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt landed for every wave (the stages issued after it may still
-    // be in flight); a bare barrier, since a full __syncthreads would also
-    // wait for those
-    if (S == 3 && kt + 1 < nk)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::DMA_PER_STAGE));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * C::DPT));
+  __builtin_amdgcn_s_barrier();
+  static_for<C::NREAD>([&](auto r) __attribute__((always_inline)) { read(r, f0, lds_base); });
+  wait_frags(f0);
+
+  auto one = [&](auto first_c, Frags<MI>& cur, Frags<MI>& nxt, int kt)
+                 __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * C::DPT));
     __builtin_amdgcn_s_barrier();
-    // refill the stage consumed in the previous iteration
-    if (kt + S - 1 < nk) issue((kt + S - 1) % S, kt + S - 1);
-    const uint32_t sa = lds_base + (kt % S) * C::STAGE_BYTES;
-    const uint32_t sb = sa + C::A_STAGE_BYTES;
-    read_frags(f0, sa, sb, std::integral_constant<int, 0>{});
-    read_frags(f1, sa, sb, std::integral_constant<int, 1>{});
-    wait_frags<C::READS_PER_KSTEP < 16 ? C::READS_PER_KSTEP : 15>(f0);
-    mfmas(f0);
-    wait_frags<0>(f1);
-    mfmas(f1);
+    const int refill_kt = kt + S < nk ? kt + S : kt;
+    step(first_c, cur, nxt, lds_base + ((kt + 1) % S) * C::STAGE_BYTES, kt % S, refill_kt);
+    wait_frags(nxt);
+  };
+  // nk is even (K is a multiple of 64): step 0, pairs (1, 2) ... (nk-3, nk-2),
+  // then step nk-1
+  one(std::true_type{}, f0, f1, 0);
+  for (int kt = 1; kt + 1 < nk; kt += 2) {
+    one(std::false_type{}, f1, f0, kt);
+    one(std::false_type{}, f0, f1, kt + 1);
   }
+  one(std::false_type{}, f1, f0, nk - 1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  // the last MFMAs' results are complete before anything else reads them
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 8; ++ni) asm volatile("" : "+a"(acc[mi][ni]));
 
   // ---------------------------------------------------- epilogue
   // acc[mi][ni]: lane (n = lane%16, g = lane/16) holds rows 4g + r of the 16x16
@@ -318,13 +377,9 @@ static hipError_t launch_tiled(const StreamGemmArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_tiled_gemm(int epi, int bm, const StreamGemmArgs& a, hipStream_t st) {
-  if (bm == 256)
-    return epi == EPI_SILU_MUL ? launch_tiled<EPI_SILU_MUL, 256>(a, st)
-                               : launch_tiled<EPI_STORE, 256>(a, st);
-  if (bm == 128)
-    return epi == EPI_SILU_MUL ? launch_tiled<EPI_SILU_MUL, 128>(a, st)
-                               : launch_tiled<EPI_STORE, 128>(a, st);
-  return hipErrorInvalidValue;
+  if (bm != 256 || a.K % 64 != 0) return hipErrorInvalidValue;
+  return epi == EPI_SILU_MUL ? launch_tiled<EPI_SILU_MUL, 256>(a, st)
+                             : launch_tiled<EPI_STORE, 256>(a, st);
 }
 
 }  // namespace moe

@@ -18,12 +18,13 @@ constexpr int ROUTER_MAX_SPLIT = 16;
 // at SPLIT_TARGET workgroups and keeps at least MIN_SPLIT_STEPS k-steps each
 // so the 4-stage load ring still streams.
 constexpr int SPLIT_BELOW = 192;
-// Average routed rows per expert from which the LDS-tiled GEMM (128-row
+// Average routed rows per expert from which the LDS-tiled GEMM (256-row
 // blocks, MFMA-bound) replaces the weight-streaming GEMM (32-row blocks).
+// 256-row blocks are used even where they pad more than 128-row ones would:
+// a 128-row block's 64 x 128 wave tiles need more LDS bytes per MFMA than the
+// LDS delivers.
 constexpr int TILED_MIN_ROWS = 64;
-// ... and from which it uses 256-row blocks (less LDS traffic per flop, more
-// padding per expert).
-constexpr int TILED_BM256_ROWS = 1024;
+constexpr int TILED_BM = 256;
 constexpr int SPLIT_TARGET = 384;
 constexpr int MIN_SPLIT_STEPS = 8;
 constexpr int64_t MAX_ENTRIES = int64_t(1) << 24;
@@ -248,7 +249,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   // regime: thick blocks go to the MFMA-tiled GEMM when its shapes fit
   const bool tiled = act == ACT_BF16 && wdt == W_BF16 && n >= (int64_t)TILED_MIN_ROWS * E &&
                      d % TILED_BN == 0 && dff % (TILED_BN / 2) == 0;
-  const int bm = !tiled ? STREAM_BM : (n >= (int64_t)TILED_BM256_ROWS * E ? 256 : 128);
+  const int bm = tiled ? TILED_BM : STREAM_BM;
   const int64_t cap = moe_align_capacity(T, E, k, bm);
   const int64_t nblocks = cap / bm;
 

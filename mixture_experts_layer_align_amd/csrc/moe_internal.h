@@ -70,8 +70,8 @@ hipError_t launch_splitk_silu(int act_dtype, const float* part, int nsplit, int6
 hipError_t launch_stream_gemm(int act_dtype, int w_dtype, int epi, const StreamGemmArgs& a,
                               hipStream_t st);
 
-// LDS-tiled MFMA grouped GEMM (thick blocks): bm-row blocks (128 or 256) x
-// 256 weight columns, bf16 activations and weights, K a multiple of 64;
+// LDS-tiled MFMA grouped GEMM (thick blocks): bm-row blocks (256) x 256
+// weight columns, bf16 activations and weights, K a multiple of 64;
 // EPI_SILU_MUL needs d_ff % 128 == 0, EPI_STORE needs n_out % 256 == 0.  No
 // k-split.
 constexpr int TILED_BN = 256;

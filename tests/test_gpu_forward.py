@@ -93,8 +93,8 @@ def test_forward_small_layers(E, k, d, d_ff, act, wdt, T, zipf):
 @pytest.mark.parametrize("T", [64, 1024])
 def test_forward_all_tokens_on_one_expert_in_full_blocks(T):
     # a one-hot bias sends every token's slot 0 to expert 3; the tokens fill
-    # whole blocks (two 32-row blocks of the streaming GEMM at T=64, eight
-    # 128-row blocks of the tiled GEMM at T=1024)
+    # whole blocks (two 32-row blocks of the streaming GEMM at T=64, four
+    # 256-row blocks of the tiled GEMM at T=1024)
     sh = LayerShape(250, "onehot", E=8, k=1, d=256, d_ff=128, act="bf16", wdt="bf16", seed=9)
     layer = make_layer(sh, T, "cuda", zipf=None)
     bias = torch.zeros(8, dtype=torch.float32, device="cuda")
@@ -104,7 +104,7 @@ def test_forward_all_tokens_on_one_expert_in_full_blocks(T):
     _, rb, bm = run_and_check(layer, x, what="one-hot")
     c = rb["counts"].cpu().numpy()
     assert c[3] == T and c.sum() == T and T % bm == 0
-    assert bm == (128 if T == 1024 else 32)
+    assert bm == (256 if T == 1024 else 32)
 
 
 def test_forward_is_deterministic():
