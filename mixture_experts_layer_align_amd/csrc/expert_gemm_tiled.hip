@@ -31,9 +31,12 @@
 //     columns hand lane i column i of those rows), two per fragment;
 //   * both LDS tiles are XOR-swizzled per row so the fragment reads hit
 //     distinct banks;
-//   * consecutive workgroups walk 8 row blocks before the next weight tile,
-//     so a weight tile is fetched from HBM once for up to 8 row blocks and a
-//     token block stays resident in its XCD's L2 across its weight tiles.
+//   * workgroups are renumbered so each of the 8 dies (one L2 each) runs a
+//     contiguous range of tiles, walking 8 row blocks before the next weight
+//     tile: the ~32 workgroups a die runs at once share their weight tiles
+//     and token blocks in its L2, and a weight tile is fetched from HBM once
+//     for up to 8 row blocks.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -47,6 +50,7 @@ namespace {
 constexpr int TBN = 256;  // weight columns per tile
 constexpr int TBK = 32;   // k per step and per LDS stage
 constexpr int GROUP_M = 8;
+constexpr int NXCD = 8;   // accelerator complex dies; workgroup i runs on die i % 8
 constexpr int B_STAGE_BYTES = TBK * TBN * 2;            // 16 KB
 constexpr int B_DPT = TBK * (TBN / 8) / 256;            // direct loads per thread: 4
 
@@ -169,18 +173,36 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---------------------------------------------------- tile of this workgroup
-  // groups of GROUP_M row blocks: row block fastest, then weight tile
-  const int id = blockIdx.x;
+  // ---------------------------------------------------- tiles of this workgroup
+  // Persistent: one workgroup per compute unit loops over the tiles of the
+  // row blocks actually in use (their count is read from the device, so no
+  // workgroups are spent on the worst-case capacity's empty blocks).  Tiles
+  // are numbered with GROUP_M row blocks walked before the next weight tile.
+  // The dispatcher deals workgroups to the dies round-robin, each die with
+  // its own L2: every die takes an equal contiguous share of that numbering,
+  // so the workgroups a die runs at once share weight tiles and token blocks
+  // in its L2 instead of each die fetching every weight tile.
+  const int n_blocks = p.padded_rows != nullptr ? min(*p.padded_rows / BM, p.num_mblocks)
+                                                : p.num_mblocks;
+  const int n_work = n_blocks * p.n_tiles;
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x % NXCD, li = blockIdx.x / NXCD;
+  const int q = nwg / NXCD, rem = nwg % NXCD;
+  const int on_die = q + (xcd < rem ? 1 : 0);
+  const int before = xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q;
+  const int w_begin = (int)((int64_t)n_work * before / nwg);
+  const int w_end = (int)((int64_t)n_work * (before + on_die) / nwg);
   const int per_group = GROUP_M * p.n_tiles;
+  for (int id = w_begin + li; id < w_end; id += on_die) {
+  // the previous tile's LDS stages are free once every wave is done with them
+  __syncthreads();
   const int grp = id / per_group;
   const int first_mb = grp * GROUP_M;
-  const int gm = min(GROUP_M, p.num_mblocks - first_mb);
+  const int gm = min(GROUP_M, n_blocks - first_mb);
   const int local = id - grp * per_group;
   const int mb = first_mb + local % gm;
   const int nt = local / gm;
   const int e = p.block_expert[mb];
-  if (e < 0) return;
   const int p0 = mb * BM;
 
   // ---------------------------------------------------- direct-load sources
@@ -361,13 +383,25 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
         for (int ni = 0; ni < 8; ++ni) dst[ni * 16] = acc[mi][ni][r];
       }
     }
+  }
+}
+
+// compute units of the current device (one resident workgroup each)
+static int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  return cus;
 }
 
 template <int EPI, int BM>
 static hipError_t launch_tiled(const StreamGemmArgs& a, hipStream_t st) {
-  const int64_t grid = (int64_t)a.num_mblocks * a.n_tiles;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int64_t work = (int64_t)a.num_mblocks * a.n_tiles;
+  if (work <= 0) return hipSuccess;
+  if (work > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int64_t grid = std::min<int64_t>(work, device_cus());
   const size_t lds = (size_t)TCfg<BM>::STAGES * TCfg<BM>::STAGE_BYTES;
   hipError_t e = hipFuncSetAttribute((const void*)k_expert_tiled<EPI, BM>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -337,6 +337,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g.topk = k;
   g.block_expert = bexp;
   g.num_mblocks = (int)nblocks;
+  g.padded_rows = offs + E;
   g.w = L->w_gate_up;
   g.w_ld = 2 * (int64_t)dff;
   g.w_estride = (int64_t)d * 2 * dff;
@@ -372,6 +373,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g2.topk = k;
   g2.block_expert = bexp;
   g2.num_mblocks = (int)nblocks;
+  g2.padded_rows = offs + E;
   g2.w = L->w_down;
   g2.w_ld = d;
   g2.w_estride = (int64_t)dff * d;

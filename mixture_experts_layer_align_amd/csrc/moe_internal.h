@@ -35,6 +35,7 @@ struct StreamGemmArgs {
   int m_total;            // A_DENSE: valid row count
   const int32_t* block_expert;  // NULL: dense, expert 0
   int num_mblocks;
+  const int32_t* padded_rows;   // tiled GEMM: device count of rows in use, or NULL (all)
   const void* w;          // weights [E][K][w_ld]
   int64_t w_ld;
   int64_t w_estride;
