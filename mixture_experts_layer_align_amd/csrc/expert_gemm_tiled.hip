@@ -25,10 +25,16 @@
 //     busy at once; one workgroup barrier per step publishes the stage that
 //     landed and frees the one just consumed;
 //   * the weight operand's K-contiguous MFMA fragments come from gfx950's
-//     transposing LDS read (ds_read_b64_tr_b16: within each 16-lane group,
-//     lane i receives element i%4 of the 8-byte pieces addressed by lanes
-//     4v + i/4, v = 0..3 — so lanes that address 4 consecutive rows x 16
-//     columns hand lane i column i of those rows), two per fragment;
+//     transposing LDS reads: bf16 weights with ds_read_b64_tr_b16 (within
+//     each 16-lane group, lane i receives element i%4 of the 8-byte pieces
+//     addressed by lanes 4v + i/4, v = 0..3 — so lanes that address 4
+//     consecutive rows x 16 columns hand lane i column i of those rows), two
+//     per fragment; fp8 (e4m3) weights with ds_read_b64_tr_b8 (lane i
+//     receives byte i%8 of the pieces addressed by lanes 2v + i/8, v = 0..7:
+//     8 rows x 16 one-byte columns), one per fragment, widened exactly to
+//     bf16 in registers; the fp8 per-column scale multiplies the fp32 sums in
+//     the epilogue (scale factored out of the dot product, the vLLM post's
+//     quantised fused-MoE statement);
 //   * both LDS tiles are XOR-swizzled per row so the fragment reads hit
 //     distinct banks;
 //   * workgroups are renumbered so each of the 8 dies (one L2 each) runs a
@@ -47,38 +53,61 @@ namespace moe {
 
 namespace {
 
+constexpr int BM = 256;   // rows per block
 constexpr int TBN = 256;  // weight columns per tile
 constexpr int TBK = 32;   // k per step and per LDS stage
 constexpr int GROUP_M = 8;
 constexpr int NXCD = 8;   // accelerator complex dies; workgroup i runs on die i % 8
-constexpr int B_STAGE_BYTES = TBK * TBN * 2;            // 16 KB
-constexpr int B_DPT = TBK * (TBN / 8) / 256;            // direct loads per thread: 4
+constexpr int MI = BM / 32;       // 16-row A fragments per wave (BM/2 rows)
+constexpr int NMFMA = MI * 8;     // MFMAs per wave per step
 
-template <int BM>
-struct TCfg {
-  static constexpr int STAGES = BM == 256 ? 4 : 6;
+// per weight type: element bytes, 16-byte chunks per weight-tile row, LDS
+// reads per fragment, stages
+template <int WT>
+struct TCfg;
+template <>
+struct TCfg<W_BF16> {
+  static constexpr int ESZ = 2, CHUNKS = 32, RD_PER_FRAG = 2, STAGES = 4;
+};
+template <>
+struct TCfg<W_FP8> {
+  static constexpr int ESZ = 1, CHUNKS = 16, RD_PER_FRAG = 1, STAGES = 6;
+};
+template <int WT>
+struct Cfg : TCfg<WT> {
+  using T = TCfg<WT>;
   static constexpr int A_STAGE_BYTES = BM * TBK * 2;
+  static constexpr int B_STAGE_BYTES = TBK * TBN * T::ESZ;
   static constexpr int STAGE_BYTES = A_STAGE_BYTES + B_STAGE_BYTES;
-  static constexpr int A_DPT = BM * (TBK / 8) / 256;   // direct loads per thread
+  static constexpr int A_DPT = A_STAGE_BYTES / (256 * 16);  // direct loads per thread
+  static constexpr int B_DPT = B_STAGE_BYTES / (256 * 16);
   static constexpr int DPT = A_DPT + B_DPT;
-  static constexpr int MI = BM / 32;                   // 16-row fragments per wave
-  static constexpr int NMFMA = MI * 8;                 // MFMAs per wave per step
-  static constexpr int NREAD = MI + 16;                // LDS reads per wave per step
-  static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
+  static constexpr int NREAD = MI + 8 * T::RD_PER_FRAG;      // LDS reads per wave per step
+  static constexpr int LDS_BYTES = T::STAGES * STAGE_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert((T::STAGES - 2) * DPT < 64, "vmcnt field");
 };
 
 constexpr int vmcnt_imm(int n) {
   return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14);
 }
 
-// swizzles: LDS chunk position of logical 16-byte chunk c in row r.
+// swizzles: LDS chunk position of logical 16-byte chunk c in row r is c ^ swz(r).
 //   A rows are 4 chunks (32 k x bf16): the 16 rows of a fragment read land in
 //   16 distinct 16-byte bank groups, and any 8 consecutive rows in 8.
-//   B rows are 32 chunks (256 columns).
+//   bf16 weight rows are 32 chunks (256 columns); fp8 weight rows 16 chunks,
+//   where r & 15 spreads the 16 rows a fragment read touches over all
+//   chunk positions.
 __device__ __forceinline__ int swz_a(int r) {
   return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
 }
-__device__ __forceinline__ int swz_b(int r) { return 2 * ((r & 3) | ((r >> 1) & 4)); }
+template <int WT>
+__device__ __forceinline__ int swz_b(int r) {
+  if constexpr (WT == W_FP8)
+    return r & 15;
+  else
+    return 2 * ((r & 3) | ((r >> 1) & 4));
+}
 
 __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
@@ -100,13 +129,66 @@ __device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
   return v;
 }
-// transposing read of 8 bytes (four 16-bit elements)
+// transposing reads of 8 bytes: four 16-bit or eight 8-bit elements
 template <int OFF>
 __device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
   static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
   u32x2 v;
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
   return v;
+}
+__device__ __forceinline__ u32x2 lds_read_tr8(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+
+// weight fragments as read from LDS
+template <int WT>
+struct BRaw {
+  u32x2 lo[8], hi[8];  // k rows 8g..8g+3 and 8g+4..8g+7 of the lane's column
+};
+template <>
+struct BRaw<W_FP8> {
+  u32x2 b8[8];  // k rows 8g..8g+7 of the lane's column, one byte each
+};
+template <int WT>
+struct Frags {
+  u32x4 a[MI];
+  BRaw<WT> b;
+};
+
+// s_waitcnt lgkmcnt(0) with the fragment registers tied to it, so nothing
+// that reads them can be scheduled before the wait
+template <int WT>
+__device__ __forceinline__ void wait_frags(Frags<WT>& f) {
+#pragma unroll
+  for (int i = 0; i < MI; ++i) asm volatile("" : "+v"(f.a[i]));
+  if constexpr (WT == W_FP8) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(f.b.b8[0]), "+v"(f.b.b8[1]), "+v"(f.b.b8[2]), "+v"(f.b.b8[3]),
+                   "+v"(f.b.b8[4]), "+v"(f.b.b8[5]), "+v"(f.b.b8[6]), "+v"(f.b.b8[7]));
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(f.b.lo[0]), "+v"(f.b.lo[1]), "+v"(f.b.lo[2]), "+v"(f.b.lo[3]),
+                   "+v"(f.b.lo[4]), "+v"(f.b.lo[5]), "+v"(f.b.lo[6]), "+v"(f.b.lo[7]),
+                   "+v"(f.b.hi[0]), "+v"(f.b.hi[1]), "+v"(f.b.hi[2]), "+v"(f.b.hi[3]),
+                   "+v"(f.b.hi[4]), "+v"(f.b.hi[5]), "+v"(f.b.hi[6]), "+v"(f.b.hi[7]));
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i) asm volatile("" : "+v"(f.a[i]));
+}
+
+// fp8 fragments widened to bf16 MFMA operands.  The widening is VALU work
+// feeding MFMAs the compiler cannot see, so the registers are tied to an
+// s_nop 1 after it: the two wait states a VALU write needs before an MFMA
+// reads the register.
+__device__ __forceinline__ void widen_fp8(const BRaw<W_FP8>& b, u32x4 (&op)[8]) {
+#pragma unroll
+  for (int ni = 0; ni < 8; ++ni) op[ni] = fp8x8_to_bf16x8(b.b8[ni]);
+  asm volatile("s_nop 1"
+               : "+v"(op[0]), "+v"(op[1]), "+v"(op[2]), "+v"(op[3]), "+v"(op[4]), "+v"(op[5]),
+                 "+v"(op[6]), "+v"(op[7]));
 }
 
 // The k-loop MFMAs are inline assembly on accumulators pinned to AGPRs
@@ -116,33 +198,14 @@ __device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
 // keeps the hazards away by construction: the accumulators are first written
 // by an MFMA with an inline-constant zero C operand (no VALU write precedes
 // an MFMA read of them), nothing but these MFMAs touches them inside the
-// loop, and s_nop padding separates the last MFMA from the epilogue's reads.
+// loop, operands written by VALU instructions are followed by s_nop padding
+// (widen_fp8), and s_nop padding separates the last MFMA from the epilogue's
+// reads.
 __device__ __forceinline__ void mfma_acc(f32x4& acc, const u32x4& a, const u32x4& b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_zero(f32x4& acc, const u32x4& a, const u32x4& b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
-}
-
-template <int MI>
-struct Frags {
-  u32x4 a[MI];
-  u32x2 bl[8], bh[8];
-};
-
-// s_waitcnt lgkmcnt(0) with the fragment registers tied to it, so nothing
-// that reads them can be scheduled before the wait
-template <int MI>
-__device__ __forceinline__ void wait_frags(Frags<MI>& f) {
-#pragma unroll
-  for (int i = 0; i < MI; ++i) asm volatile("" : "+v"(f.a[i]));
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(f.bl[0]), "+v"(f.bl[1]), "+v"(f.bl[2]), "+v"(f.bl[3]), "+v"(f.bl[4]),
-                 "+v"(f.bl[5]), "+v"(f.bl[6]), "+v"(f.bl[7]), "+v"(f.bh[0]), "+v"(f.bh[1]),
-                 "+v"(f.bh[2]), "+v"(f.bh[3]), "+v"(f.bh[4]), "+v"(f.bh[5]), "+v"(f.bh[6]),
-                 "+v"(f.bh[7]));
-#pragma unroll
-  for (int i = 0; i < MI; ++i) asm volatile("" : "+v"(f.a[i]));
 }
 
 template <int I>
@@ -163,15 +226,19 @@ constexpr int slot_of(int i, int n, int span) { return (i * span) / n; }
 
 }  // namespace
 
-template <int EPI, int BM>
+template <int EPI, int WT>
 __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
-  using C = TCfg<BM>;
+  using C = Cfg<WT>;
   constexpr int S = C::STAGES;
-  constexpr int MI = C::MI;
+  constexpr int ESZ = C::ESZ;
+  constexpr int CH = C::CHUNKS;    // 16-byte chunks per weight-tile row
+  constexpr int EPC = 16 / ESZ;    // weight elements per chunk
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
+  const int lm = lane & 15, lg = lane >> 4;
+  const uint32_t lds_base = lds_off(lds);
 
   // ---------------------------------------------------- tiles of this workgroup
   // Persistent: one workgroup per compute unit loops over the tiles of the
@@ -193,6 +260,7 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
   const int w_begin = (int)((int64_t)n_work * before / nwg);
   const int w_end = (int)((int64_t)n_work * (before + on_die) / nwg);
   const int per_group = GROUP_M * p.n_tiles;
+  const int nk = p.K / TBK;
   for (int id = w_begin + li; id < w_end; id += on_die) {
   // the previous tile's LDS stages are free once every wave is done with them
   __syncthreads();
@@ -218,22 +286,23 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
     const int c = (lane & 3) ^ swz_a(r);
     a_src[i] = reinterpret_cast<const char*>(p.a) + ((int64_t)row * p.a_ld + 8 * c) * 2;
   }
-  // B slot s = (wave*B_DPT + i)*64 + lane -> k row s/32, position s%32
-  const char* b_src[B_DPT];
+  // B slot s = (wave*B_DPT + i)*64 + lane -> k row s/CH, position s%CH; for
+  // gate|up the first half of a row's chunks are the h-tile's gate columns,
+  // the second half the matching up columns
+  const char* b_src[C::B_DPT];
 #pragma unroll
-  for (int i = 0; i < B_DPT; ++i) {
-    const int r = (wave * B_DPT + i) * 2 + (lane >> 5);
-    const int c = (lane & 31) ^ swz_b(r);
+  for (int i = 0; i < C::B_DPT; ++i) {
+    const int r = (wave * C::B_DPT + i) * (64 / CH) + lane / CH;
+    const int c = (lane % CH) ^ swz_b<WT>(r);
     int col;
     if constexpr (EPI == EPI_SILU_MUL)
-      col = (c < 16) ? nt * 128 + 8 * c : p.up_off + nt * 128 + 8 * (c - 16);
+      col = (c < CH / 2) ? nt * 128 + EPC * c : p.up_off + nt * 128 + EPC * (c - CH / 2);
     else
-      col = nt * TBN + 8 * c;
+      col = nt * TBN + EPC * c;
     b_src[i] = reinterpret_cast<const char*>(p.w) +
-               ((int64_t)e * p.w_estride + (int64_t)r * p.w_ld + col) * 2;
+               ((int64_t)e * p.w_estride + (int64_t)r * p.w_ld + col) * ESZ;
   }
-  const int64_t b_kstep = (int64_t)TBK * p.w_ld * 2;  // bytes per k-step of B
-  const int nk = p.K / TBK;
+  const int64_t b_kstep = (int64_t)TBK * p.w_ld * ESZ;  // bytes per k-step of B
 
   // the d-th direct load (of DPT) of k-step kt into stage st
   auto dma = [&](auto d_c, int st, int kt) __attribute__((always_inline)) {
@@ -243,7 +312,7 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
       dma16(a_src[d] + (int64_t)kt * (TBK * 2), sa + (wave * C::A_DPT + d) * 1024);
     } else {
       constexpr int i = d - C::A_DPT;
-      dma16(b_src[i] + kt * b_kstep, sa + C::A_STAGE_BYTES + (wave * B_DPT + i) * 1024);
+      dma16(b_src[i] + kt * b_kstep, sa + C::A_STAGE_BYTES + (wave * C::B_DPT + i) * 1024);
     }
   };
   auto dma_all = [&](int st, int kt) __attribute__((always_inline)) {
@@ -254,65 +323,84 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
   // A fragment mi: row R = wm*BM/2 + mi*16 + lane%16, chunk lane/16.
   // R%16 = lane%16, so the swizzle is the lane's own and the address is a
   // per-lane base plus the immediate mi*1024.
-  const int lm = lane & 15, lg = lane >> 4;
-  const uint32_t lds_base = lds_off(lds);
   const uint32_t a_base = (uint32_t)(((wm * (BM / 2) + lm) * 4 + (lg ^ swz_a(lm))) * 16);
-  // B fragment ni, half h: k row 8*lg + lm/4 + 4h, chunk c0(ni) + (lm%4)/2,
-  // 8-byte half lm&1.  swz_b of that row depends only on lm/4 and lg&1, so
-  // it is the lane's own; h is an immediate.
-  const int xb = swz_b(8 * lg + (lm >> 2));
+  // B fragment ni covers chunk c0(ni) (fp8: 16 columns) or chunks c0(ni),
+  // c0(ni)+1 (bf16) of the wave's columns.
+  //   bf16, half h: k row 8*lg + lm/4 + 4h, chunk c0 + (lm%4)/2, 8-byte half
+  //   lm&1; swz of that row depends only on lm/4 and lg&1 (the lane's own),
+  //   h is the immediate 4 rows.
+  //   fp8: k row 8*lg + lm/2, chunk c0, 8-byte half lm&1.
   uint32_t b_base[8];
 #pragma unroll
   for (int ni = 0; ni < 8; ++ni) {
-    int c0;
-    if constexpr (EPI == EPI_SILU_MUL)
-      c0 = ni < 4 ? 2 * (wn * 4 + ni) : 16 + 2 * (wn * 4 + ni - 4);
-    else
-      c0 = 2 * (wn * 8 + ni);
-    const int row = 8 * lg + (lm >> 2);
-    b_base[ni] = (uint32_t)((row * 32 + ((c0 ^ xb) + ((lm & 3) >> 1))) * 16 + (lm & 1) * 8) +
-                 C::A_STAGE_BYTES;
+    if constexpr (WT == W_FP8) {
+      int c0;
+      if constexpr (EPI == EPI_SILU_MUL)
+        c0 = ni < 4 ? wn * 4 + ni : 8 + wn * 4 + (ni - 4);
+      else
+        c0 = wn * 8 + ni;
+      const int row = 8 * lg + (lm >> 1);
+      b_base[ni] = (uint32_t)((row * CH + (c0 ^ swz_b<WT>(row))) * 16 + (lm & 1) * 8) +
+                   C::A_STAGE_BYTES;
+    } else {
+      int c0;
+      if constexpr (EPI == EPI_SILU_MUL)
+        c0 = ni < 4 ? 2 * (wn * 4 + ni) : 16 + 2 * (wn * 4 + ni - 4);
+      else
+        c0 = 2 * (wn * 8 + ni);
+      const int row = 8 * lg + (lm >> 2);
+      const int xb = swz_b<WT>(row);
+      b_base[ni] = (uint32_t)((row * CH + ((c0 ^ xb) + ((lm & 3) >> 1))) * 16 + (lm & 1) * 8) +
+                   C::A_STAGE_BYTES;
+    }
   }
 
   // r-th fragment read (of NREAD) of the stage at LDS offset st_off into f
-  auto read = [&](auto r_c, Frags<MI>& f, uint32_t st_off) __attribute__((always_inline)) {
+  auto read = [&](auto r_c, Frags<WT>& f, uint32_t st_off) __attribute__((always_inline)) {
     constexpr int r = decltype(r_c)::value;
     if constexpr (r < MI) {
       f.a[r] = lds_read_b128<r * 1024>(st_off + a_base);
+    } else if constexpr (WT == W_FP8) {
+      f.b.b8[r - MI] = lds_read_tr8(st_off + b_base[r - MI]);
     } else {
       constexpr int ni = (r - MI) >> 1;
       if constexpr (((r - MI) & 1) == 0)
-        f.bl[ni] = lds_read_tr16<0>(st_off + b_base[ni]);
+        f.b.lo[ni] = lds_read_tr16<0>(st_off + b_base[ni]);
       else
-        f.bh[ni] = lds_read_tr16<4 * 512>(st_off + b_base[ni]);
+        f.b.hi[ni] = lds_read_tr16<4 * CH * 16>(st_off + b_base[ni]);
     }
   };
 
   f32x4 acc[MI][8];
+  // fp8: bf16 weight operands of the current and the next step
+  u32x4 w0[WT == W_FP8 ? 8 : 1], w1[WT == W_FP8 ? 8 : 1];
 
-  // One k-step: MFMAs on `cur`; between them, the reads of `nxt` from the
-  // stage at nxt_off (within the first 3/4 of the MFMAs, so they land before
-  // the step ends) and the direct loads of k-step refill_kt into stage
-  // refill_st.  Every op is pinned where it stands.  FIRST: the accumulators
-  // start from zero.
-  auto step = [&](auto first_c, Frags<MI>& cur, Frags<MI>& nxt, uint32_t nxt_off, int refill_st,
-                  int refill_kt) __attribute__((always_inline)) {
+  // One k-step: MFMAs on `cur` (fp8: on the widened `wcur`); between them,
+  // the reads of `nxt` from the stage at nxt_off (within the first 3/4 of the
+  // MFMAs, so they land before the step ends) and the direct loads of k-step
+  // refill_kt into stage refill_st.  Every op is pinned where it stands.
+  // FIRST: the accumulators start from zero.
+  auto step = [&](auto first_c, Frags<WT>& cur, const u32x4* wcur, Frags<WT>& nxt,
+                  uint32_t nxt_off, int refill_st, int refill_kt) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_c)::value;
-    constexpr int NM = C::NMFMA;
-    static_for<NM>([&](auto i_c) __attribute__((always_inline)) {
+    static_for<NMFMA>([&](auto i_c) __attribute__((always_inline)) {
       constexpr int i = decltype(i_c)::value;
       constexpr int ni = i / MI, mi = i % MI;
-      const u32x4 bf = {cur.bl[ni][0], cur.bl[ni][1], cur.bh[ni][0], cur.bh[ni][1]};
+      u32x4 bf;
+      if constexpr (WT == W_FP8)
+        bf = wcur[ni];
+      else
+        bf = u32x4{cur.b.lo[ni][0], cur.b.lo[ni][1], cur.b.hi[ni][0], cur.b.hi[ni][1]};
       if constexpr (FIRST)
         mfma_zero(acc[mi][ni], cur.a[mi], bf);
       else
         mfma_acc(acc[mi][ni], cur.a[mi], bf);
       static_for<C::NREAD>([&](auto r_c) __attribute__((always_inline)) {
-        if constexpr (slot_of(decltype(r_c)::value, C::NREAD, (3 * NM) / 4) == i)
+        if constexpr (slot_of(decltype(r_c)::value, C::NREAD, (3 * NMFMA) / 4) == i)
           read(r_c, nxt, nxt_off);
       });
       static_for<C::DPT>([&](auto d_c) __attribute__((always_inline)) {
-        if constexpr (slot_of(decltype(d_c)::value, C::DPT, NM) == i)
+        if constexpr (slot_of(decltype(d_c)::value, C::DPT, NMFMA) == i)
           dma(d_c, refill_st, refill_kt);
       });
       __builtin_amdgcn_sched_barrier(0);
@@ -330,28 +418,30 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
   // always in flight.
 #pragma unroll
   for (int s = 0; s < S; ++s) dma_all(s, s < nk ? s : 0);
-  Frags<MI> f0, f1;
+  Frags<WT> f0, f1;
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * C::DPT));
   __builtin_amdgcn_s_barrier();
   static_for<C::NREAD>([&](auto r) __attribute__((always_inline)) { read(r, f0, lds_base); });
   wait_frags(f0);
+  if constexpr (WT == W_FP8) widen_fp8(f0.b, w0);
 
-  auto one = [&](auto first_c, Frags<MI>& cur, Frags<MI>& nxt, int kt)
-                 __attribute__((always_inline)) {
+  auto one = [&](auto first_c, Frags<WT>& cur, const u32x4* wcur, Frags<WT>& nxt,
+                 u32x4* wnxt, int kt) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * C::DPT));
     __builtin_amdgcn_s_barrier();
     const int refill_kt = kt + S < nk ? kt + S : kt;
-    step(first_c, cur, nxt, lds_base + ((kt + 1) % S) * C::STAGE_BYTES, kt % S, refill_kt);
+    step(first_c, cur, wcur, nxt, lds_base + ((kt + 1) % S) * C::STAGE_BYTES, kt % S, refill_kt);
     wait_frags(nxt);
+    if constexpr (WT == W_FP8) widen_fp8(nxt.b, *reinterpret_cast<u32x4(*)[8]>(wnxt));
   };
   // nk is even (K is a multiple of 64): step 0, pairs (1, 2) ... (nk-3, nk-2),
   // then step nk-1
-  one(std::true_type{}, f0, f1, 0);
+  one(std::true_type{}, f0, w0, f1, w1, 0);
   for (int kt = 1; kt + 1 < nk; kt += 2) {
-    one(std::false_type{}, f1, f0, kt);
-    one(std::false_type{}, f0, f1, kt + 1);
+    one(std::false_type{}, f1, w1, f0, w0, kt);
+    one(std::false_type{}, f0, w0, f1, w1, kt + 1);
   }
-  one(std::false_type{}, f1, f0, nk - 1);
+  one(std::false_type{}, f1, w1, f0, w0, nk - 1);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   // the last MFMAs' results are complete before anything else reads them
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -362,7 +452,20 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
 
   // ---------------------------------------------------- epilogue
   // acc[mi][ni]: lane (n = lane%16, g = lane/16) holds rows 4g + r of the 16x16
-  // block (mi, ni)
+  // block (mi, ni).  Lane columns: gate|up ni < 4: gate column
+  // nt*128 + wn*64 + 16ni + lm, ni >= 4 the matching up column; down:
+  // nt*256 + wn*128 + 16ni + lm.
+  float sc[8];  // fp8: per-column scales of the lane's 8 columns
+  if constexpr (WT == W_FP8) {
+    const float* sb = p.scale + (int64_t)e * p.scale_estride;
+#pragma unroll
+    for (int ni = 0; ni < 8; ++ni) {
+      if constexpr (EPI == EPI_SILU_MUL)
+        sc[ni] = sb[(ni < 4 ? 0 : p.up_off) + nt * 128 + wn * 64 + 16 * (ni & 3) + lm];
+      else
+        sc[ni] = sb[nt * TBN + wn * 128 + 16 * ni + lm];
+    }
+  }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -374,13 +477,21 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
         uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + prow * p.out_ld + nt * 128 + wn * 64 + lm;
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-          const float hv = silu(acc[mi][ni][r]) * acc[mi][ni + 4][r];
-          dst[ni * 16] = (uint16_t)f32_to_bf16_bits(hv);
+          float g = acc[mi][ni][r], u = acc[mi][ni + 4][r];
+          if constexpr (WT == W_FP8) {
+            g *= sc[ni];
+            u *= sc[ni + 4];
+          }
+          dst[ni * 16] = (uint16_t)f32_to_bf16_bits(silu(g) * u);
         }
       } else {
         float* dst = reinterpret_cast<float*>(p.out) + prow * p.out_ld + nt * TBN + wn * 128 + lm;
 #pragma unroll
-        for (int ni = 0; ni < 8; ++ni) dst[ni * 16] = acc[mi][ni][r];
+        for (int ni = 0; ni < 8; ++ni) {
+          float v = acc[mi][ni][r];
+          if constexpr (WT == W_FP8) v *= sc[ni];
+          dst[ni * 16] = v;
+        }
       }
     }
   }
@@ -388,32 +499,44 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
 
 // compute units of the current device (one resident workgroup each)
 static int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     return 256;
+  if (dev >= 0 && dev < 64) cached[dev] = cus;
   return cus;
 }
 
-template <int EPI, int BM>
+template <int EPI, int WT>
 static hipError_t launch_tiled(const StreamGemmArgs& a, hipStream_t st) {
   const int64_t work = (int64_t)a.num_mblocks * a.n_tiles;
   if (work <= 0) return hipSuccess;
   if (work > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int64_t grid = std::min<int64_t>(work, device_cus());
-  const size_t lds = (size_t)TCfg<BM>::STAGES * TCfg<BM>::STAGE_BYTES;
-  hipError_t e = hipFuncSetAttribute((const void*)k_expert_tiled<EPI, BM>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  constexpr int lds = Cfg<WT>::LDS_BYTES;
+  hipError_t e = hipFuncSetAttribute((const void*)k_expert_tiled<EPI, WT>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_expert_tiled<EPI, BM>), dim3((unsigned)grid), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((k_expert_tiled<EPI, WT>), dim3((unsigned)grid), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_tiled_gemm(int epi, int bm, const StreamGemmArgs& a, hipStream_t st) {
-  if (bm != 256 || a.K % 64 != 0) return hipErrorInvalidValue;
-  return epi == EPI_SILU_MUL ? launch_tiled<EPI_SILU_MUL, 256>(a, st)
-                             : launch_tiled<EPI_STORE, 256>(a, st);
+hipError_t launch_tiled_gemm(int epi, int w_dtype, int bm, const StreamGemmArgs& a,
+                             hipStream_t st) {
+  if (bm != BM || a.K % 64 != 0) return hipErrorInvalidValue;
+  if (w_dtype == W_FP8) {
+    if (a.scale == nullptr) return hipErrorInvalidValue;
+    return epi == EPI_SILU_MUL ? launch_tiled<EPI_SILU_MUL, W_FP8>(a, st)
+                               : launch_tiled<EPI_STORE, W_FP8>(a, st);
+  }
+  if (w_dtype == W_BF16)
+    return epi == EPI_SILU_MUL ? launch_tiled<EPI_SILU_MUL, W_BF16>(a, st)
+                               : launch_tiled<EPI_STORE, W_BF16>(a, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

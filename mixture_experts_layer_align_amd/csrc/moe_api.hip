@@ -247,7 +247,8 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   const int ab = act_bytes(L->act_dtype);
   const int64_t n = (int64_t)T * k;
   // regime: thick blocks go to the MFMA-tiled GEMM when its shapes fit
-  const bool tiled = act == ACT_BF16 && wdt == W_BF16 && n >= (int64_t)TILED_MIN_ROWS * E &&
+  const bool tiled = act == ACT_BF16 && (wdt == W_BF16 || wdt == W_FP8) &&
+                     n >= (int64_t)TILED_MIN_ROWS * E &&
                      d % TILED_BN == 0 && dff % (TILED_BN / 2) == 0;
   const int bm = tiled ? TILED_BM : STREAM_BM;
   const int64_t cap = moe_align_capacity(T, E, k, bm);
@@ -355,7 +356,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g.out = h;
   g.out_ld = dff;
   trace_mark(tr, &kidx, "gate_up", st);
-  e = tiled ? launch_tiled_gemm(EPI_SILU_MUL, bm, g, st)
+  e = tiled ? launch_tiled_gemm(EPI_SILU_MUL, wdt, bm, g, st)
             : launch_stream_gemm(act, wdt, EPI_SILU_MUL, g, st);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   if (gu_split > 1) {
@@ -390,7 +391,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g2.out = y;
   g2.out_ld = d;
   trace_mark(tr, &kidx, "down", st);
-  e = tiled ? launch_tiled_gemm(EPI_STORE, bm, g2, st)
+  e = tiled ? launch_tiled_gemm(EPI_STORE, wdt, bm, g2, st)
             : launch_stream_gemm(act, wdt, EPI_STORE, g2, st);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
 

@@ -72,11 +72,12 @@ hipError_t launch_stream_gemm(int act_dtype, int w_dtype, int epi, const StreamG
                               hipStream_t st);
 
 // LDS-tiled MFMA grouped GEMM (thick blocks): bm-row blocks (256) x 256
-// weight columns, bf16 activations and weights, K a multiple of 64;
+// weight columns, bf16 activations, bf16 or fp8 weights, K a multiple of 64;
 // EPI_SILU_MUL needs d_ff % 128 == 0, EPI_STORE needs n_out % 256 == 0.  No
 // k-split.
 constexpr int TILED_BN = 256;
-hipError_t launch_tiled_gemm(int epi, int bm, const StreamGemmArgs& a, hipStream_t st);
+hipError_t launch_tiled_gemm(int epi, int w_dtype, int bm, const StreamGemmArgs& a,
+                             hipStream_t st);
 
 // Router logits: A_DENSE rows, weights [K, n_out] with any n_out; split s writes
 // the fp32 plane out + s * out_split_stride.

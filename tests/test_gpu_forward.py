@@ -77,6 +77,10 @@ SMALL = [
     (8, 2, 512, 384, "bf16", "bf16", 700, 1.2),      # skewed, ragged blocks
     (1, 1, 256, 128, "bf16", "bf16", 200, None),     # one expert, 2 blocks
     (16, 4, 768, 640, "bf16", "bf16", 1111, 0.8),
+    # ... with fp8 weights (scales applied to the fp32 sums)
+    (4, 2, 256, 512, "bf16", "fp8", 400, None),
+    (16, 4, 512, 256, "bf16", "fp8", 700, 1.0),      # skewed, ragged blocks
+    (2, 1, 768, 256, "bf16", "fp8", 600, None),      # 24 k-steps of gate|up
 ]
 
 
