@@ -497,25 +497,12 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
   }
 }
 
-// compute units of the current device (one resident workgroup each)
-static int device_cus() {
-  static int cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    return 256;
-  if (dev >= 0 && dev < 64) cached[dev] = cus;
-  return cus;
-}
-
 template <int EPI, int WT>
 static hipError_t launch_tiled(const StreamGemmArgs& a, hipStream_t st) {
   const int64_t work = (int64_t)a.num_mblocks * a.n_tiles;
   if (work <= 0) return hipSuccess;
   if (work > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // one resident workgroup per compute unit
   const int64_t grid = std::min<int64_t>(work, device_cus());
   constexpr int lds = Cfg<WT>::LDS_BYTES;
   hipError_t e = hipFuncSetAttribute((const void*)k_expert_tiled<EPI, WT>,

@@ -14,9 +14,9 @@ constexpr int64_t WS_ALIGN = 256;
 constexpr int ROUTER_TARGET_WGS = 512;
 constexpr int ROUTER_MAX_SPLIT = 16;
 // Expert GEMMs split K only when the blocks x n-tiles work items leave the chip
-// under-filled (fewer than SPLIT_BELOW two-wave workgroups); a split then aims
-// at SPLIT_TARGET workgroups and keeps at least MIN_SPLIT_STEPS k-steps each
-// so the 4-stage load ring still streams.
+// under-filled (fewer than SPLIT_BELOW two-wave workgroups); the split then
+// balances the compute units (choose_kchunk_balanced) and keeps at least
+// MIN_SPLIT_STEPS k-steps each so the 4-stage load ring still streams.
 constexpr int SPLIT_BELOW = 192;
 // Average routed rows per expert from which the LDS-tiled GEMM (256-row
 // blocks, MFMA-bound) replaces the weight-streaming GEMM (32-row blocks).
@@ -25,7 +25,6 @@ constexpr int SPLIT_BELOW = 192;
 // LDS delivers.
 constexpr int TILED_MIN_ROWS = 64;
 constexpr int TILED_BM = 256;
-constexpr int SPLIT_TARGET = 384;
 constexpr int MIN_SPLIT_STEPS = 8;
 constexpr int64_t MAX_ENTRIES = int64_t(1) << 24;
 
@@ -76,6 +75,32 @@ int choose_kchunk(int64_t items, int K, int kstep, int* nsplit, int below, int t
                                 (int64_t)max_split});
   s = std::max(s, 1);
   const int chunk_steps = (steps + s - 1) / s;
+  *nsplit = (steps + chunk_steps - 1) / chunk_steps;
+  return chunk_steps * kstep;
+}
+
+// Number of k-splits for a weight-streaming GEMM of `items` workgroups when
+// fewer than `below` would run: every split adds a workgroup per item, and
+// the layer takes as long as its busiest compute unit, whose share of the
+// work is ceil(items*s / cus) / s (workgroups of equal size, spread evenly).
+// The smallest s with the least share wins; at least min_steps k-steps each.
+int choose_kchunk_balanced(int64_t items, int K, int kstep, int* nsplit, int below, int min_steps,
+                           int max_split, int cus) {
+  const int steps = K / kstep;
+  items = std::max<int64_t>(items, 1);
+  int best = 1;
+  if (items < below) {
+    const int smax = std::max(1, std::min(max_split, steps / min_steps));
+    double best_cost = 1e30;
+    for (int s = 1; s <= smax; ++s) {
+      const double cost = (double)((items * s + cus - 1) / cus) / s;
+      if (cost < best_cost * (1.0 - 1e-9)) {
+        best_cost = cost;
+        best = s;
+      }
+    }
+  }
+  const int chunk_steps = (steps + best - 1) / best;
   *nsplit = (steps + chunk_steps - 1) / chunk_steps;
   return chunk_steps * kstep;
 }
@@ -148,6 +173,21 @@ int validate_route(int T, int d, int E, int k, int act) {
 }
 
 }  // namespace
+
+namespace moe {
+int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  if (dev >= 0 && dev < 64) cached[dev] = cus;
+  return cus;
+}
+}  // namespace moe
 
 extern "C" {
 
@@ -267,10 +307,11 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
       std::min<int64_t>(nblocks, std::max<int64_t>(std::min<int64_t>(E, n), (n + bm - 1) / bm));
   int gu_split = 1, dn_split = 1, gu_chunk = d, dn_chunk = dff;
   if (!tiled) {
-    gu_chunk = choose_kchunk(std::max<int64_t>(est_blocks, 1) * gu_tiles, d, kstep, &gu_split,
-                             SPLIT_BELOW, SPLIT_TARGET, MIN_SPLIT_STEPS, 64);
-    dn_chunk = choose_kchunk(std::max<int64_t>(est_blocks, 1) * dn_tiles, dff, kstep, &dn_split,
-                             SPLIT_BELOW, SPLIT_TARGET, MIN_SPLIT_STEPS, 64);
+    const int cus = device_cus();
+    gu_chunk = choose_kchunk_balanced(std::max<int64_t>(est_blocks, 1) * gu_tiles, d, kstep,
+                                      &gu_split, SPLIT_BELOW, MIN_SPLIT_STEPS, 64, cus);
+    dn_chunk = choose_kchunk_balanced(std::max<int64_t>(est_blocks, 1) * dn_tiles, dff, kstep,
+                                      &dn_split, SPLIT_BELOW, MIN_SPLIT_STEPS, 64, cus);
   }
   Carve c(workspace);
   float* r_partial = c.take<float>(std::max<int64_t>(r.partial_floats, 1));

@@ -55,6 +55,10 @@ struct StreamGemmArgs {
   int64_t out_split_stride;  // router: elements between split planes
 };
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails).
+int device_cus();
+
 // Rows per m-block of the stream GEMM (two 16-row MFMA column groups).
 constexpr int STREAM_BM = 32;
 
