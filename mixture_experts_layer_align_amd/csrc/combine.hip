@@ -13,7 +13,7 @@
 
 namespace moe {
 
-template <int ACT>
+template <int ACT, int JB>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, int nsplit,
                                                  int64_t split_stride,
                                                  const int32_t* __restrict__ inv_pos,
@@ -28,22 +28,41 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, in
     float acc[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const float wj = wt[j];
-      const float* row = y + (int64_t)ip[j] * d + c0;
-      float ys[VEC];
+    // JB slots at a time (JB >= k up to 8): every row load of the batch is
+    // issued before any of them is added, so a token costs ~k/JB memory round
+    // trips, not 2k
+    for (int j0 = 0; j0 < k; j0 += JB) {
+      int pos[JB];
+      float wj[JB];
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) ys[v] = 0.f;
+      for (int jj = 0; jj < JB; ++jj) {
+        const bool ok = j0 + jj < k;
+        pos[jj] = ip[ok ? j0 + jj : 0];  // past k: slot 0 again, never added
+        wj[jj] = ok ? wt[j0 + jj] : 0.f;
+      }
+      float ys[JB][VEC];
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) ys[jj][v] = 0.f;
       for (int s = 0; s < nsplit; ++s) {
 #pragma unroll
-        for (int h = 0; h < VEC / 4; ++h) {
-          const u32x4 r = ld16(row + s * split_stride + 4 * h);
+        for (int jj = 0; jj < JB; ++jj) {
+          const float* row = y + (int64_t)pos[jj] * d + c0 + s * split_stride;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) ys[4 * h + q] += __uint_as_float(r[q]);
+          for (int h = 0; h < VEC / 4; ++h) {
+            const u32x4 r = ld16(row + 4 * h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ys[jj][4 * h + q] += __uint_as_float(r[q]);
+          }
         }
       }
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[v] += wj * ys[v];
+      for (int jj = 0; jj < JB; ++jj)
+        if (j0 + jj < k) {
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[v] += wj[jj] * ys[jj][v];
+        }
     }
     u32x4 o;
     if constexpr (ACT == ACT_BF16) {
@@ -64,12 +83,22 @@ hipError_t launch_combine(int act, const float* y, int nsplit, int64_t split_str
   if (T == 0) return hipSuccess;
   const int vec = act == ACT_BF16 ? 8 : 4;
   const dim3 grid((unsigned)T, (unsigned)((d + 256 * vec - 1) / (256 * vec)));
-  if (act == ACT_BF16)
-    hipLaunchKernelGGL(k_combine<ACT_BF16>, grid, dim3(256), 0, st, y, nsplit, split_stride,
-                       inv_pos, w, k, d, reinterpret_cast<char*>(out));
-  else
-    hipLaunchKernelGGL(k_combine<ACT_F32>, grid, dim3(256), 0, st, y, nsplit, split_stride,
-                       inv_pos, w, k, d, reinterpret_cast<char*>(out));
+  const int jb = k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : 8;
+#define MOE_COMBINE(A_, JB_)                                                                  \
+  hipLaunchKernelGGL((k_combine<A_, JB_>), grid, dim3(256), 0, st, y, nsplit, split_stride, \
+                     inv_pos, w, k, d, reinterpret_cast<char*>(out))
+  if (act == ACT_BF16) {
+    if (jb == 1) MOE_COMBINE(ACT_BF16, 1);
+    else if (jb == 2) MOE_COMBINE(ACT_BF16, 2);
+    else if (jb == 4) MOE_COMBINE(ACT_BF16, 4);
+    else MOE_COMBINE(ACT_BF16, 8);
+  } else {
+    if (jb == 1) MOE_COMBINE(ACT_F32, 1);
+    else if (jb == 2) MOE_COMBINE(ACT_F32, 2);
+    else if (jb == 4) MOE_COMBINE(ACT_F32, 4);
+    else MOE_COMBINE(ACT_F32, 8);
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

@@ -11,8 +11,12 @@ using namespace moe;
 namespace {
 
 constexpr int64_t WS_ALIGN = 256;
-constexpr int ROUTER_TARGET_WGS = 512;
-constexpr int ROUTER_MAX_SPLIT = 16;
+// Router GEMM: split d until ~ROUTER_TARGET_WGS two-wave workgroups run, at
+// most ROUTER_MAX_SPLIT planes and ROUTER_MIN_STEPS k-steps per split (the
+// loads run 3 steps ahead).
+constexpr int ROUTER_TARGET_WGS = 1024;
+constexpr int ROUTER_MAX_SPLIT = 32;
+constexpr int ROUTER_MIN_STEPS = 4;
 // Expert GEMMs split K only when the blocks x n-tiles work items leave the chip
 // under-filled (fewer than SPLIT_BELOW two-wave workgroups); the split then
 // balances the compute units (choose_kchunk_balanced) and keeps at least
@@ -129,7 +133,8 @@ RouterPlan plan_router(const void* x, const void* w_router, int T, int d, int E,
   const int tc = router_tile_cols(act);
   g.n_tiles = (E + tc - 1) / tc;
   g.kchunk = choose_kchunk((int64_t)g.num_mblocks * g.n_tiles, d, router_kstep(act), &g.ksplit,
-                           ROUTER_TARGET_WGS, ROUTER_TARGET_WGS, 2, ROUTER_MAX_SPLIT);
+                           ROUTER_TARGET_WGS, ROUTER_TARGET_WGS, ROUTER_MIN_STEPS,
+                           ROUTER_MAX_SPLIT);
   g.out_ld = E;
   g.out_split_stride = (int64_t)T * E;
   r.nsplit = g.ksplit;

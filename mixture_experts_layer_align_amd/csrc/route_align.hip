@@ -35,33 +35,98 @@ __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
 }
 
+// Router partial planes are added in one fixed order whatever the launch
+// shape: four interleaved sums (planes q, q+4, q+8, ... in plane order, for
+// q = 0..3), then ((s0 + s1) + s2) + s3.  All V values of a plane are loaded
+// together and planes are unrolled, so many loads are in flight (slots past
+// E read expert E-1, in bounds, and are discarded).
 template <int V>
+__device__ __forceinline__ void plane_sums(const float* __restrict__ pp, int nsplit,
+                                           int64_t split_stride, int E, int lane,
+                                           float (&acc)[4][V]) {
+  int eo[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) eo[j] = min(lane + 64 * j, E - 1);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[q][j] = 0.f;
+  for (int base = 0; base < nsplit; base += 4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (base + q >= nsplit) continue;
+      const float* p = pp + (base + q) * split_stride;
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[q][j] += p[eo[j]];
+    }
+  }
+}
+// the interleaved sum q alone (planes q, q+4, ...)
+template <int V>
+__device__ __forceinline__ void plane_sum_q(const float* __restrict__ pp, int nsplit,
+                                            int64_t split_stride, int E, int lane, int q,
+                                            float (&acc)[V]) {
+  int eo[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    eo[j] = min(lane + 64 * j, E - 1);
+    acc[j] = 0.f;
+  }
+#pragma unroll 4
+  for (int sp = q; sp < nsplit; sp += 4) {
+    const float* p = pp + sp * split_stride;
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[j] += p[eo[j]];
+  }
+}
+
+// Top-k of one token per wave (tokens = 4 per workgroup) or, with WIDE, of
+// one token per workgroup whose 4 waves each own one of the 4 plane sums.
+template <int V, bool WIDE>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial, int nsplit,
                                               int64_t split_stride, const float* __restrict__ bias,
                                               int T, int E, int k, float* __restrict__ logits,
                                               int32_t* __restrict__ ids, float* __restrict__ wout) {
-  __shared__ float sel_v[4][MAX_EXPERTS];
-  __shared__ int sel_i[4][MAX_EXPERTS];
+  __shared__ float part[WIDE ? 4 : 1][WIDE ? MAX_EXPERTS : 1];
+  __shared__ float sel_v[WIDE ? 1 : 4][MAX_EXPERTS];
+  __shared__ int sel_i[WIDE ? 1 : 4][MAX_EXPERTS];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
+  const int t = WIDE ? blockIdx.x : blockIdx.x * 4 + wave;
   if (t >= T) return;
+  const float* pp = partial + (int64_t)t * E;
 
   float v[V];
+  if constexpr (WIDE) {
+    float acc[V];
+    plane_sum_q<V>(pp, nsplit, split_stride, E, lane, wave, acc);
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+      if (lane + 64 * j < E) part[wave][lane + 64 * j] = acc[j];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int e = min(lane + 64 * j, E - 1);
+      v[j] = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
+    }
+  } else {
+    float acc[4][V];
+    plane_sums<V>(pp, nsplit, split_stride, E, lane, acc);
+#pragma unroll
+    for (int j = 0; j < V; ++j) v[j] = ((acc[0][j] + acc[1][j]) + acc[2][j]) + acc[3][j];
+  }
+  const int sw = WIDE ? 0 : wave;
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const int e = lane + 64 * j;
-    float s = -INFINITY;
     if (e < E) {
-      const float* pp = partial + (int64_t)t * E + e;
-      s = pp[0];
-#pragma unroll 4
-      for (int sp = 1; sp < nsplit; ++sp) s += pp[sp * split_stride];
-      if (bias != nullptr) s += bias[e];
-      if (logits != nullptr) logits[(int64_t)t * E + e] = s;
+      if (bias != nullptr) v[j] += bias[e];
+      if (logits != nullptr) logits[(int64_t)t * E + e] = v[j];
+    } else {
+      v[j] = -INFINITY;
     }
-    v[j] = s;
   }
 
   for (int r = 0; r < k; ++r) {
@@ -88,30 +153,39 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial,
         if (bi == lane + 64 * j) v[j] = -INFINITY;
     }
     if (lane == 0) {
-      sel_v[wave][r] = bv;
-      sel_i[wave][r] = bi;
+      sel_v[sw][r] = bv;
+      sel_i[sw][r] = bi;
     }
   }
   // weights: exp(L_j - L_0) / sum, the sum as a fixed butterfly
-  const float l0 = sel_v[wave][0];
-  float part = 0.f;
-  for (int r = lane; r < k; r += 64) part += expf(sel_v[wave][r] - l0);
+  const float l0 = sel_v[sw][0];
+  float psum = 0.f;
+  for (int r = lane; r < k; r += 64) psum += expf(sel_v[sw][r] - l0);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-  const float inv = 1.0f / part;
+  for (int off = 32; off >= 1; off >>= 1) psum += __shfl_xor(psum, off);
+  const float inv = 1.0f / psum;
   for (int r = lane; r < k; r += 64) {
-    ids[(int64_t)t * k + r] = sel_i[wave][r];
-    wout[(int64_t)t * k + r] = expf(sel_v[wave][r] - l0) * inv;
+    ids[(int64_t)t * k + r] = sel_i[sw][r];
+    wout[(int64_t)t * k + r] = expf(sel_v[sw][r] - l0) * inv;
   }
 }
 
+// tokens from which one wave per token fills the chip better than a
+// workgroup per token
+constexpr int TOPK_WIDE_MAX_T = 1024;
+
 hipError_t launch_topk(const float* partial, int nsplit, int64_t split_stride, const float* bias,
                        int T, int E, int k, float* logits, int32_t* ids, float* w, hipStream_t st) {
-  const int grid = (T + 3) / 4;
-  if (grid == 0) return hipSuccess;
-#define MOE_TOPK(V_)                                                                           \
-  hipLaunchKernelGGL(k_topk<V_>, dim3(grid), dim3(256), 0, st, partial, nsplit, split_stride, \
-                     bias, T, E, k, logits, ids, w)
+  if (T == 0) return hipSuccess;
+  const bool wide = T <= TOPK_WIDE_MAX_T;
+  const int grid = wide ? T : (T + 3) / 4;
+#define MOE_TOPK(V_)                                                                            \
+  if (wide)                                                                                     \
+    hipLaunchKernelGGL((k_topk<V_, true>), dim3(grid), dim3(256), 0, st, partial, nsplit,        \
+                       split_stride, bias, T, E, k, logits, ids, w);                             \
+  else                                                                                          \
+    hipLaunchKernelGGL((k_topk<V_, false>), dim3(grid), dim3(256), 0, st, partial, nsplit,       \
+                       split_stride, bias, T, E, k, logits, ids, w)
   if (E <= 64) MOE_TOPK(1);
   else if (E <= 128) MOE_TOPK(2);
   else if (E <= 256) MOE_TOPK(4);

@@ -11,7 +11,7 @@
 // because E need not be a multiple of the 16-byte chunk: columns past E are
 // read element by element and zero-filled.  A workgroup is two waves, each
 // streaming one 128-column slab (bf16; 64 for fp32) of its k-range for a block
-// of 32 tokens.
+// of 32 tokens, with its loads running three k-steps ahead of its MFMAs.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -100,33 +100,52 @@ __global__ __launch_bounds__(128) void k_router_gemm(const StreamGemmArgs p) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[q][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (ocol - lg * NV < p.n_out) {
-    for (int k0 = kb; k0 < ke; k0 += KSTEP) {
-      u32x4 raw[RPL];
+  // k-steps of this split; loads run DEPTH steps ahead of the MFMAs in a
+  // register ring (clamped past the end: reloads of the last step, in bounds
+  // and never used), so a workgroup is not bound by one memory latency per
+  // step
+  const int nsteps = (ke - kb) / KSTEP;
+  if (ocol - lg * NV < p.n_out && nsteps > 0) {
+    constexpr int DEPTH = 3;
+    u32x4 raw[DEPTH][RPL], xv[DEPTH][2];
+    auto load = [&](int d, int step) __attribute__((always_inline)) {
+      const int k0 = kb + min(step, nsteps - 1) * KSTEP;
       const char* base = w + (int64_t)(k0 + lg * RPL) * wrow_bytes;
 #pragma unroll
-      for (int j = 0; j < RPL; ++j) raw[j] = load_wrow<WT>(base + j * wrow_bytes, wcol, p.n_out, vec_ok);
-      u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+      for (int j = 0; j < RPL; ++j) raw[d][j] = load_wrow<WT>(base + j * wrow_bytes, wcol, p.n_out, vec_ok);
       const int kk = k0 + (WT == W_BF16 ? 8 : 4) * lg;
-      if (rvalid[0]) x0 = ld16(arow[0] + (int64_t)kk * ASZ);
-      if (rvalid[1]) x1 = ld16(arow[1] + (int64_t)kk * ASZ);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      xv[d][0] = rvalid[0] ? ld16(arow[0] + (int64_t)kk * ASZ) : z;
+      xv[d][1] = rvalid[1] ? ld16(arow[1] + (int64_t)kk * ASZ) : z;
+    };
+    auto compute = [&](int d) __attribute__((always_inline)) {
+      const u32x4 x0 = xv[d][0], x1 = xv[d][1];
       if constexpr (WT == W_F32) {
 #pragma unroll
         for (int ss = 0; ss < 4; ++ss)
 #pragma unroll
           for (int c = 0; c < CPL; ++c) {
-            const float a = __uint_as_float(raw[ss][c]);
+            const float a = __uint_as_float(raw[d][ss][c]);
             acc[0][c] = mfma_f32_16x16x4(a, __uint_as_float(x0[ss]), acc[0][c]);
             if (use_q1) acc[1][c] = mfma_f32_16x16x4(a, __uint_as_float(x1[ss]), acc[1][c]);
           }
       } else {
         u32x4 frag[8];
-        transpose8x8_b16(raw, frag);
+        transpose8x8_b16(raw[d], frag);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
           acc[0][c] = mfma_bf16_16x16x32(frag[c], x0, acc[0][c]);
           if (use_q1) acc[1][c] = mfma_bf16_16x16x32(frag[c], x1, acc[1][c]);
         }
+      }
+    };
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d) load(d, d);
+    for (int it = 0; it < nsteps; it += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        load((d + DEPTH - 1) % DEPTH, it + d + DEPTH - 1);
+        if (it + d < nsteps) compute(d);
       }
     }
   }
