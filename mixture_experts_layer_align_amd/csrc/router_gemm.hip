@@ -43,6 +43,7 @@ __device__ __forceinline__ u32x4 load_wrow(const char* rowp, int col, int n_vali
   constexpr int CPL = RTr<WT>::CPL;
   if (vec_ok && col + CPL <= n_valid) return ld16(rowp + (int64_t)col * RTr<WT>::ESIZE);
   u32x4 v = {0u, 0u, 0u, 0u};
+  if (col >= n_valid) return v;  // wholly past E: nothing to read
   if constexpr (WT == W_BF16) {
     const uint16_t* h = reinterpret_cast<const uint16_t*>(rowp);
     for (int c = 0; c < CPL; ++c)
