@@ -18,7 +18,8 @@
 //     the block (weight-stationary); a 16-row group with no routed row is
 //     skipped;
 //   * weights go HBM -> LDS with direct loads (global_load_lds_dwordx4: no
-//     VGPR holds data in flight) through a 4-stage ring per wave, 8 KB a stage;
+//     VGPR holds data in flight) through a ring of 8 KB stages per wave (two
+//     for bf16, four for fp8);
 //     each lane reads back exactly the 16-byte chunks it requested (8
 //     consecutive weight rows, 16 lanes covering 256 contiguous bytes of a row)
 //     and transposes its 8x8 bf16 block in registers (v_perm_b32) into 8 MFMA A
@@ -28,6 +29,9 @@
 //     permuted activations are never materialised (the pages copy tokens into
 //     padded per-expert buffers first: "CuTeDSL at Perplexity", MoE dispatch
 //     and combine, local kernel);
+//   * bf16 weights with more items than compute units: a persistent grid of
+//     at most one workgroup per compute unit, each taking an equal share of
+//     whole items (measured faster than one workgroup per item);
 //   * when blocks x n-tiles cannot fill the chip, K is split: each split stores
 //     fp32 partial sums and the next kernel adds them in split order (fixed
 //     order, no atomics, no device-scope fences: on gfx950 a device-scope
@@ -46,6 +50,8 @@
 // columns), converts them exactly to bf16 in registers and runs the same bf16
 // MFMA (activations stay bf16).  fp32 weights: 4 columns per lane, no
 // transpose, v_mfma_f32_16x16x4_f32.
+#include <algorithm>
+
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -77,7 +83,14 @@ struct DTr<W_F32> {
   static constexpr int ESIZE = 4;
 };
 
-constexpr int STAGES = 4;
+// Load-ring stages per wave.  bf16: two — with fewer requests outstanding
+// HBM serves the weight stream faster (more stages measured slower on gfx950).
+// fp8: four — its heavier per-stage math needs the deeper ring, and the
+// larger LDS footprint keeps two workgroups per compute unit.
+template <int WT>
+constexpr int stages_of() {
+  return WT == W_BF16 ? 2 : 4;
+}
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
 // operations of this wave are outstanding; LDS/scalar and export counters are
@@ -92,8 +105,9 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
 
 }  // namespace
 
+// One item = (32-row block, n-tile, k-split) of the launch.
 template <int ACT, int WT, int EPI>
-__global__ __launch_bounds__(128) void k_expert_stream(const StreamGemmArgs p) {
+__device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32x4* lds) {
   using Tr = DTr<WT>;
   constexpr int CPL = Tr::CPL;
   constexpr int RPL = Tr::RPL;
@@ -102,20 +116,15 @@ __global__ __launch_bounds__(128) void k_expert_stream(const StreamGemmArgs p) {
   constexpr int NV = 4 * CPL;     // contiguous output columns per lane
   constexpr int ASZ = (ACT == ACT_BF16) ? 2 : 4;
   constexpr int XK = (ACT == ACT_BF16) ? 8 : 4;  // k-values per lane per token fragment
-  constexpr int S = STAGES;
+  constexpr int S = stages_of<WT>();
   constexpr int PER = RPL + 2;    // vector-memory ops per stage: weight rows + 2 token loads
   static_assert((S - 1) * PER <= 63, "vmcnt field");
-
-  // ring[wave][stage][row][lane]; after the main loop the same memory holds
-  // the epilogue exchange
-  __shared__ u32x4 lds[2 * S * RPL * WAVE];
 
   const int lane = threadIdx.x & 63;
   const int slab = threadIdx.x >> 6;
   const int li = lane & 15;  // MFMA column within a 16-group (token row)
   const int lg = lane >> 4;  // k group
 
-  int id = blockIdx.x;
   const int split = id % p.ksplit;
   id /= p.ksplit;
   const int nt = id % p.n_tiles;
@@ -323,6 +332,25 @@ __global__ __launch_bounds__(128) void k_expert_stream(const StreamGemmArgs p) {
   }
 }
 
+// Workgroup g takes items g, g + gridDim.x, ...: with as many workgroups as
+// compute units and an equal share each, the weight stream runs with one
+// front per expert group and no partly filled last round.  Items are numbered
+// n-tile fastest, so the blocks in use (a prefix of the m-blocks) make a
+// prefix of the items.
+template <int ACT, int WT, int EPI>
+__global__ __launch_bounds__(128) void k_expert_stream(const StreamGemmArgs p) {
+  // ring[wave][stage][row][lane]; after an item's main loop the same memory
+  // holds its epilogue exchange
+  __shared__ u32x4 lds[2 * stages_of<WT>() * DTr<WT>::RPL * WAVE];
+  int blocks = p.num_mblocks;
+  if (p.padded_rows != nullptr) blocks = min(blocks, *p.padded_rows / STREAM_BM);
+  const int items = blocks * p.n_tiles * p.ksplit;
+  for (int i = blockIdx.x; i < items; i += gridDim.x) {
+    __syncthreads();  // the previous item's epilogue is done with the ring
+    stream_item<ACT, WT, EPI>(p, i, lds);
+  }
+}
+
 // h[p, n] = SiLU(sum_s g_s[p, n]) * sum_s u_s[p, n] for the routed rows p,
 // splits added in order.  One workgroup per (row, 2048-column chunk).
 template <int ACT>
@@ -383,9 +411,10 @@ int stream_kstep(int w_dtype) {
 
 template <int ACT, int WT, int EPI>
 static hipError_t launch_one(const StreamGemmArgs& a, hipStream_t st) {
-  const int64_t grid = (int64_t)a.num_mblocks * a.n_tiles * a.ksplit;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int64_t items = (int64_t)a.num_mblocks * a.n_tiles * a.ksplit;
+  if (items <= 0) return hipSuccess;
+  if (items > 0x7FFFFFFF || a.wgs < 0) return hipErrorInvalidValue;
+  const int64_t grid = a.wgs > 0 ? std::min<int64_t>(a.wgs, items) : items;
   hipLaunchKernelGGL((k_expert_stream<ACT, WT, EPI>), dim3((unsigned)grid), dim3(128), 0, st, a);
   return hipGetLastError();
 }

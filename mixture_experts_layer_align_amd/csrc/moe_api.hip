@@ -88,6 +88,16 @@ int choose_kchunk(int64_t items, int K, int kstep, int* nsplit, int below, int t
 // the layer takes as long as its busiest compute unit, whose share of the
 // work is ceil(items*s / cus) / s (workgroups of equal size, spread evenly).
 // The smallest s with the least share wins; at least min_steps k-steps each.
+// Workgroups of a persistent stream GEMM launch over `items` expected items:
+// as many as leave every workgroup the same whole number of items, at most
+// one per compute unit; 0 (one workgroup per item) when there are fewer items
+// than compute units.
+int persistent_wgs(int64_t items, int cus) {
+  if (items <= cus) return 0;
+  const int64_t per = (items + cus - 1) / cus;
+  return (int)((items + per - 1) / per);
+}
+
 int choose_kchunk_balanced(int64_t items, int K, int kstep, int* nsplit, int below, int min_steps,
                            int max_split, int cus) {
   const int steps = K / kstep;
@@ -310,13 +320,22 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   // blocks expected to carry rows: one per active expert plus the overflow
   const int64_t est_blocks =
       std::min<int64_t>(nblocks, std::max<int64_t>(std::min<int64_t>(E, n), (n + bm - 1) / bm));
-  int gu_split = 1, dn_split = 1, gu_chunk = d, dn_chunk = dff;
+  int gu_split = 1, dn_split = 1, gu_chunk = d, dn_chunk = dff, gu_wgs = 0, dn_wgs = 0;
   if (!tiled) {
     const int cus = device_cus();
-    gu_chunk = choose_kchunk_balanced(std::max<int64_t>(est_blocks, 1) * gu_tiles, d, kstep,
-                                      &gu_split, SPLIT_BELOW, MIN_SPLIT_STEPS, 64, cus);
-    dn_chunk = choose_kchunk_balanced(std::max<int64_t>(est_blocks, 1) * dn_tiles, dff, kstep,
-                                      &dn_split, SPLIT_BELOW, MIN_SPLIT_STEPS, 64, cus);
+    const int64_t gu_items = std::max<int64_t>(est_blocks, 1) * gu_tiles;
+    const int64_t dn_items = std::max<int64_t>(est_blocks, 1) * dn_tiles;
+    gu_chunk = choose_kchunk_balanced(gu_items, d, kstep, &gu_split, SPLIT_BELOW, MIN_SPLIT_STEPS,
+                                      64, cus);
+    dn_chunk = choose_kchunk_balanced(dn_items, dff, kstep, &dn_split, SPLIT_BELOW,
+                                      MIN_SPLIT_STEPS, 64, cus);
+    // bf16 weights stream fastest with one workgroup per compute unit; fp8
+    // weights (twice the math per byte) need the latency hiding of several
+    // workgroups per compute unit and keep one workgroup per item
+    if (wdt == W_BF16) {
+      gu_wgs = persistent_wgs(gu_items * gu_split, cus);
+      dn_wgs = persistent_wgs(dn_items * dn_split, cus);
+    }
   }
   Carve c(workspace);
   float* r_partial = c.take<float>(std::max<int64_t>(r.partial_floats, 1));
@@ -396,6 +415,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g.n_tiles = gu_tiles;
   g.ksplit = gu_split;
   g.kchunk = gu_chunk;
+  g.wgs = gu_wgs;
   g.partial = gu_part;
   g.partial_ld = 2 * (int64_t)dff;
   g.partial_split_stride = cap * 2 * dff;
@@ -431,6 +451,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g2.n_tiles = dn_tiles;
   g2.ksplit = dn_split;
   g2.kchunk = dn_chunk;
+  g2.wgs = dn_wgs;
   g2.partial = y;
   g2.partial_ld = d;
   g2.partial_split_stride = cap * d;

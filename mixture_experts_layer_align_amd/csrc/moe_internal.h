@@ -35,7 +35,7 @@ struct StreamGemmArgs {
   int m_total;            // A_DENSE: valid row count
   const int32_t* block_expert;  // NULL: dense, expert 0
   int num_mblocks;
-  const int32_t* padded_rows;   // tiled GEMM: device count of rows in use, or NULL (all)
+  const int32_t* padded_rows;   // device count of rows in use, or NULL (all)
   const void* w;          // weights [E][K][w_ld]
   int64_t w_ld;
   int64_t w_estride;
@@ -53,6 +53,8 @@ struct StreamGemmArgs {
   void* out;
   int64_t out_ld;
   int64_t out_split_stride;  // router: elements between split planes
+  int wgs;                // stream GEMM: workgroups, each looping over items
+                          //   g, g + wgs, ...; 0 = one workgroup per item
 };
 
 // Compute units of the current device (cached per device; 256 if the query
