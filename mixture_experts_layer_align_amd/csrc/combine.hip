@@ -8,6 +8,11 @@
 // with 16-byte loads (first adding a row's k-split partial sums, in split
 // order, when the down GEMM was split) and sums them in fp32 in slot order
 // j = 0..k-1, then rounds once to the activation dtype.
+//
+// Few tokens (decode) leave most compute units idle with that shape, and each
+// workgroup walks the k-splits one memory round trip after another.  There a
+// one-wave workgroup covers 256 elements (4 per lane) and every row load of
+// NS splits x JB slots is issued before the first add.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -77,6 +82,87 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, in
   }
 }
 
+template <int ACT, int JB, int NS>
+__global__ __launch_bounds__(64) void k_combine_narrow(const float* __restrict__ y, int nsplit,
+                                                       int64_t split_stride,
+                                                       const int32_t* __restrict__ inv_pos,
+                                                       const float* __restrict__ w, int k, int d,
+                                                       char* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  const int32_t* ip = inv_pos + t * k;
+  const float* wt = w + t * k;
+  const int c0 = (blockIdx.y * 64 + threadIdx.x) * 4;
+  if (c0 >= d) return;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < k; j0 += JB) {
+    int pos[JB];
+    float wj[JB];
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+      const bool ok = j0 + jj < k;
+      pos[jj] = ip[ok ? j0 + jj : 0];  // past k: slot 0 again, never added
+      wj[jj] = ok ? wt[j0 + jj] : 0.f;
+    }
+    float ys[JB][4];
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) ys[jj][v] = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += NS) {
+      // NS splits per pass; a split past the last reloads the last and is
+      // not added (splits are still added in order)
+      u32x4 r[NS][JB];
+#pragma unroll
+      for (int q = 0; q < NS; ++q) {
+        const int64_t so = (int64_t)min(s0 + q, nsplit - 1) * split_stride;
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) r[q][jj] = ld16(y + so + (int64_t)pos[jj] * d + c0);
+      }
+#pragma unroll
+      for (int q = 0; q < NS; ++q)
+        if (s0 + q < nsplit) {
+#pragma unroll
+          for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) ys[jj][v] += __uint_as_float(r[q][jj][v]);
+        }
+    }
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj)
+      if (j0 + jj < k) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] += wj[jj] * ys[jj][v];
+      }
+  }
+  if constexpr (ACT == ACT_BF16) {
+    const u32x2 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *reinterpret_cast<u32x2*>(out + (t * d + c0) * 2) = o;
+  } else {
+    const u32x4 o = {__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                     __float_as_uint(acc[3])};
+    st16(out + (t * d + c0) * 4, o);
+  }
+}
+
+// Token x 2048-element chunks below which the one-wave variant is used.
+constexpr int NARROW_BELOW = 256;
+
+template <int ACT, int JB>
+static void launch_narrow(const float* y, int nsplit, int64_t split_stride, const int32_t* inv_pos,
+                          const float* w, int T, int k, int d, void* out, hipStream_t st) {
+  const dim3 grid((unsigned)T, (unsigned)((d + 255) / 256));
+  char* o = reinterpret_cast<char*>(out);
+  if (nsplit >= 4)
+    hipLaunchKernelGGL((k_combine_narrow<ACT, JB, 4>), grid, dim3(64), 0, st, y, nsplit,
+                       split_stride, inv_pos, w, k, d, o);
+  else if (nsplit >= 2)
+    hipLaunchKernelGGL((k_combine_narrow<ACT, JB, 2>), grid, dim3(64), 0, st, y, nsplit,
+                       split_stride, inv_pos, w, k, d, o);
+  else
+    hipLaunchKernelGGL((k_combine_narrow<ACT, JB, 1>), grid, dim3(64), 0, st, y, nsplit,
+                       split_stride, inv_pos, w, k, d, o);
+}
+
 hipError_t launch_combine(int act, const float* y, int nsplit, int64_t split_stride,
                           const int32_t* inv_pos, const float* w, int T, int k, int d, void* out,
                           hipStream_t st) {
@@ -84,6 +170,22 @@ hipError_t launch_combine(int act, const float* y, int nsplit, int64_t split_str
   const int vec = act == ACT_BF16 ? 8 : 4;
   const dim3 grid((unsigned)T, (unsigned)((d + 256 * vec - 1) / (256 * vec)));
   const int jb = k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : 8;
+  if ((int64_t)T * ((d + 2047) / 2048) < NARROW_BELOW) {
+#define MOE_NARROW(A_, JB_) launch_narrow<A_, JB_>(y, nsplit, split_stride, inv_pos, w, T, k, d, out, st)
+    if (act == ACT_BF16) {
+      if (jb == 1) MOE_NARROW(ACT_BF16, 1);
+      else if (jb == 2) MOE_NARROW(ACT_BF16, 2);
+      else if (jb == 4) MOE_NARROW(ACT_BF16, 4);
+      else MOE_NARROW(ACT_BF16, 8);
+    } else {
+      if (jb == 1) MOE_NARROW(ACT_F32, 1);
+      else if (jb == 2) MOE_NARROW(ACT_F32, 2);
+      else if (jb == 4) MOE_NARROW(ACT_F32, 4);
+      else MOE_NARROW(ACT_F32, 8);
+    }
+#undef MOE_NARROW
+    return hipGetLastError();
+  }
 #define MOE_COMBINE(A_, JB_)                                                                  \
   hipLaunchKernelGGL((k_combine<A_, JB_>), grid, dim3(256), 0, st, y, nsplit, split_stride, \
                      inv_pos, w, k, d, reinterpret_cast<char*>(out))

@@ -15,7 +15,6 @@ constexpr int64_t WS_ALIGN = 256;
 // most ROUTER_MAX_SPLIT planes and ROUTER_MIN_STEPS k-steps per split (the
 // loads run 3 steps ahead).
 constexpr int ROUTER_TARGET_WGS = 1024;
-constexpr int ROUTER_MAX_SPLIT = 32;
 constexpr int ROUTER_MIN_STEPS = 4;
 // Expert GEMMs split K only when the blocks x n-tiles work items leave the chip
 // under-filled (fewer than SPLIT_BELOW two-wave workgroups); the split then
@@ -374,10 +373,6 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   hipStream_t st = static_cast<hipStream_t>(stream);
   int kidx = 0;
 
-  hipError_t e = run_router(r, act, r_partial, L->logit_bias, T, E, k, logits, ids, tw, st, tr,
-                            &kidx);
-  if (e != hipSuccess) return MOE_ERR_DEVICE;
-
   AlignArgs a{};
   a.ids = ids;
   a.n = (int)n;
@@ -391,9 +386,24 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   a.sorted_ids = sorted;
   a.inv_pos = inv;
   a.block_expert = bexp;
-  trace_mark(tr, &kidx, "align", st);
-  e = launch_align(a, al_ws, st);
-  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  hipError_t e;
+  if (route_align_small_ok(T, E, k, r.nsplit)) {
+    // a few tokens: top-k and alignment in one launch
+    r.g.out = r_partial;
+    trace_mark(tr, &kidx, "router_gemm", st);
+    e = launch_router_gemm(act, r.g, st);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    trace_mark(tr, &kidx, "route_align", st);
+    e = launch_route_align_small(r_partial, r.nsplit, (int64_t)T * E, L->logit_bias, logits, ids,
+                                 tw, a, st);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+  } else {
+    e = run_router(r, act, r_partial, L->logit_bias, T, E, k, logits, ids, tw, st, tr, &kidx);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    trace_mark(tr, &kidx, "align", st);
+    e = launch_align(a, al_ws, st);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+  }
 
   StreamGemmArgs g{};
   g.a = x;

@@ -122,6 +122,18 @@ constexpr int ALIGN_TILE = 4096;         // entries per tile of the multi-pass p
 int64_t align_workspace_bytes(int n, int E);
 hipError_t launch_align(AlignArgs a, void* ws, hipStream_t st);
 
+// Router: at most this many fp32 partial planes over d.
+constexpr int ROUTER_MAX_SPLIT = 32;
+
+// Top-k of the router planes and the alignment in one single-workgroup launch
+// (ids receives the ids; a.ids is not read); for T <= 16, E <= 256, k <= 64.
+inline bool route_align_small_ok(int T, int E, int k, int nsplit) {
+  return T >= 1 && T <= 16 && E <= 256 && k <= 64 && nsplit >= 1 && nsplit <= ROUTER_MAX_SPLIT;
+}
+hipError_t launch_route_align_small(const float* partial, int nsplit, int64_t split_stride,
+                                    const float* bias, float* logits, int32_t* ids, float* w,
+                                    const AlignArgs& a, hipStream_t st);
+
 // ------------------------------------------------------------ combine
 
 // y: per-slot expert outputs, fp32 [nsplit][cap, d] (k-split partial sums,

@@ -311,15 +311,15 @@ __device__ __forceinline__ int ilog2_ceil(int E) {
   return b;
 }
 
-// One workgroup aligns all entries (n <= ALIGN_TILE).
-__global__ __launch_bounds__(AL_THREADS) void k_align_single(const AlignArgs a) {
-  extern __shared__ int lds[];
+// One workgroup aligns all entries (n <= ALIGN_TILE) of `ids` (global or
+// LDS memory); lds holds AL_WAVES * E + 2 * E + 1 + AL_WAVES + 1 ints.
+__device__ void align_one_tile(const AlignArgs& a, const int32_t* ids, int* lds) {
   int* hist = lds;                          // [AL_WAVES][E]
   int* s_counts = hist + AL_WAVES * a.E;    // [E]
   int* s_off = s_counts + a.E;              // [E + 1]
   int* sh = s_off + a.E + 1;                // [AL_WAVES + 1]
   const int E = a.E;
-  const ChunkState cs = tile_local_ranks(a.ids, 0, a.n, E, ilog2_ceil(E), hist);
+  const ChunkState cs = tile_local_ranks(ids, 0, a.n, E, ilog2_ceil(E), hist);
   const int cnt = hist_wave_prefix(hist, E);
   int padded = 0;
   if ((int)threadIdx.x < E) padded = (cnt + a.bm - 1) / a.bm * a.bm;
@@ -342,6 +342,151 @@ __global__ __launch_bounds__(AL_THREADS) void k_align_single(const AlignArgs a) 
     a.inv_pos[i] = pos;
   }
   write_layout(a, s_counts, s_off);
+}
+
+__global__ __launch_bounds__(AL_THREADS) void k_align_single(const AlignArgs a) {
+  extern __shared__ int lds[];
+  align_one_tile(a, a.ids, lds);
+}
+
+// ================================================================ small batch
+// Routing and alignment of a few tokens (T <= AL_WAVES) in one launch: wave t
+// routes token t exactly as k_topk does (same plane order, same selection
+// and weight arithmetic, so the same bits), keeping its k <= 64 selections in
+// lane registers; the ids also go to LDS, from where the workgroup aligns
+// them as k_align_single does.  One launch and one global round trip fewer.
+
+// Plane loads in batches of NB planes (64 values a lane), each batch issued
+// before its adds (planes past nsplit reload the last plane and are not
+// added); sums in the order of plane_sums.
+template <int V, int NSMAX>
+__device__ __forceinline__ void plane_sums_all(const float* __restrict__ pp, int nsplit,
+                                               int64_t split_stride, int E, int lane,
+                                               float (&acc)[4][V]) {
+  constexpr int NB = (64 / V < NSMAX) ? 64 / V : NSMAX;
+  static_assert(NB % 4 == 0 && NSMAX % NB == 0, "batches keep the plane order");
+  int eo[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) eo[j] = min(lane + 64 * j, E - 1);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[q][j] = 0.f;
+#pragma unroll
+  for (int b0 = 0; b0 < NSMAX; b0 += NB) {
+    if (b0 >= nsplit) break;
+    float val[NB][V];
+#pragma unroll
+    for (int sp = 0; sp < NB; ++sp) {
+      const float* p = pp + (int64_t)min(b0 + sp, nsplit - 1) * split_stride;
+#pragma unroll
+      for (int j = 0; j < V; ++j) val[sp][j] = p[eo[j]];
+    }
+#pragma unroll
+    for (int sp = 0; sp < NB; ++sp)
+      if (b0 + sp < nsplit) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) acc[sp & 3][j] += val[sp][j];
+      }
+  }
+}
+
+template <int V>
+__global__ __launch_bounds__(AL_THREADS) void k_route_align_small(
+    const float* __restrict__ partial, int nsplit, int64_t split_stride,
+    const float* __restrict__ bias, float* __restrict__ logits, int32_t* __restrict__ ids,
+    float* __restrict__ wout, const AlignArgs a) {
+  extern __shared__ int lds[];
+  int* s_ids = lds;             // [n]
+  int* al = lds + a.n;          // alignment scratch
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int E = a.E, k = a.k;
+  if (wave < a.T) {
+    const int t = wave;
+    float acc[4][V];
+    plane_sums_all<V, ROUTER_MAX_SPLIT>(partial + (int64_t)t * E, nsplit, split_stride, E, lane,
+                                        acc);
+    float v[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      v[j] = ((acc[0][j] + acc[1][j]) + acc[2][j]) + acc[3][j];
+      const int e = lane + 64 * j;
+      if (e < E) {
+        if (bias != nullptr) v[j] += bias[e];
+        if (logits != nullptr) logits[(int64_t)t * E + e] = v[j];
+      } else {
+        v[j] = -INFINITY;
+      }
+    }
+    float myv = 0.f, l0 = 0.f;
+    int myi = 0;
+    for (int r = 0; r < k; ++r) {
+      float bv = v[0];
+      int bi = lane;
+#pragma unroll
+      for (int j = 1; j < V; ++j)
+        if (better(v[j], lane + 64 * j, bv, bi)) {
+          bv = v[j];
+          bi = lane + 64 * j;
+        }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & 63) == lane) {
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+          if (bi == lane + 64 * j) v[j] = -INFINITY;
+      }
+      if (r == 0) l0 = bv;
+      if (lane == r) {
+        myv = bv;
+        myi = bi;
+      }
+    }
+    float psum = lane < k ? expf(myv - l0) : 0.f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) psum += __shfl_xor(psum, off);
+    const float inv = 1.0f / psum;
+    if (lane < k) {
+      const int64_t o = (int64_t)t * k + lane;
+      ids[o] = myi;
+      wout[o] = expf(myv - l0) * inv;
+      s_ids[o] = myi;
+    }
+  }
+  __syncthreads();
+  align_one_tile(a, s_ids, al);
+}
+
+hipError_t launch_route_align_small(const float* partial, int nsplit, int64_t split_stride,
+                                    const float* bias, float* logits, int32_t* ids, float* w,
+                                    const AlignArgs& a, hipStream_t st) {
+  if (a.T <= 0) return hipSuccess;
+  if (!route_align_small_ok(a.T, a.E, a.k, nsplit)) return hipErrorInvalidValue;
+  const size_t lds =
+      ((size_t)a.n + (size_t)AL_WAVES * a.E + 2 * a.E + 1 + AL_WAVES + 1) * sizeof(int);
+#define MOE_RAS(V_)                                                                           \
+  do {                                                                                        \
+    if (lds > 65536) {                                                                        \
+      hipError_t e_ = hipFuncSetAttribute((const void*)k_route_align_small<V_>,               \
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (e_ != hipSuccess) return e_;                                                        \
+    }                                                                                         \
+    hipLaunchKernelGGL((k_route_align_small<V_>), dim3(1), dim3(AL_THREADS), lds, st, partial, \
+                       nsplit, split_stride, bias, logits, ids, w, a);                             \
+  } while (0)
+  if (a.E <= 64) MOE_RAS(1);
+  else if (a.E <= 128) MOE_RAS(2);
+  else MOE_RAS(4);
+#undef MOE_RAS
+  return hipGetLastError();
 }
 
 // Multi-tile pass 1: per-tile histogram and rank of each entry in its tile.
