@@ -5,6 +5,12 @@ SiLU*up epilogue, down GEMM, weighted combine) over one batch of synthetic
 tokens of the decode layer E=8, top-2, d=4096, d_ff=14336, bf16, with weights
 and tokens already resident in HBM.  Prints one JSON line.
 
+Infinity-Cache guard: MI355X keeps up to 256 MB of recently read lines in its
+memory-side cache, so a layer whose active weights are small would be timed
+from that cache when the same weights are read step after step.  Timed loops
+therefore cycle through R copies of the weights, R chosen so that one cycle
+reads at least 1 GiB of layer bytes.
+
   python bench.py [--steps K] [--warmup W] [--tokens T] [--config C]
 """
 import argparse
@@ -32,6 +38,32 @@ def parse():
     return ap.parse_args()
 
 
+GUARD_BYTES = 1 << 30
+MAX_REPLICAS = 32
+
+
+def guarded_forwards(B, roof, layer, bias, sh, x, T):
+    """Forward objects over R copies of the layer's weights (R >= 1 chosen so
+    that one cycle reads >= GUARD_BYTES), the routing of the first call, and
+    the number of active experts."""
+    import torch
+    f0 = B.Forward(layer.w_router, bias, layer.w_gate_up, layer.w_down, sh.k,
+                   layer.scale_gate_up, layer.scale_down)
+    rb = f0.routing_buffers(T)
+    f0(x, routing=rb)
+    torch.cuda.synchronize()
+    active = int((rb["counts"].cpu().numpy() > 0).sum())
+    work = roof.layer_work(T, sh.d, sh.d_ff, sh.E, sh.k, sh.act, sh.wdt, active)
+    reps = max(1, min(MAX_REPLICAS, -(-GUARD_BYTES // max(int(work.bytes_total), 1))))
+    fwds = [f0]
+    for _ in range(reps - 1):
+        c = (lambda t: None if t is None else t.clone())
+        fwds.append(B.Forward(c(layer.w_router), bias, c(layer.w_gate_up), c(layer.w_down), sh.k,
+                              c(layer.scale_gate_up), c(layer.scale_down)))
+    torch.cuda.synchronize()
+    return fwds, rb, active, work
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -53,47 +85,40 @@ def main():
     torch.cuda.set_device(dev)
     layer = make_layer(sh, None, dev, zipf=None)
     bias = make_bias(sh, sh.zipf_for(T), dev)
-    fwd = B.Forward(layer.w_router, bias, layer.w_gate_up, layer.w_down, sh.k,
-                    layer.scale_gate_up, layer.scale_down)
     stream = torch.cuda.current_stream()
 
-    def timed(x, steps, warmup):
+    def timed(fwds, x, steps, warmup):
         out = torch.empty_like(x)
-        for _ in range(warmup):
-            fwd(x, out)
+        for i in range(warmup):
+            fwds[i % len(fwds)](x, out)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(stream)
-        for _ in range(steps):
-            fwd(x, out)
+        for i in range(steps):
+            fwds[i % len(fwds)](x, out)
         t1.record(stream)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / steps, out
 
     x = make_tokens(sh, T, dev)
-    torch.cuda.synchronize()
-    ms, out = timed(x, args.steps, args.warmup)
+    fwds, rb, active, work = guarded_forwards(B, R, layer, bias, sh, x, T)
+    ms, out = timed(fwds, x, args.steps, args.warmup)
 
     # per-kernel durations, HIP events recorded on the launch stream between
     # the kernels of each forward
-    rb = fwd.routing_buffers(T)
-    _, bm, names = fwd(x, routing=rb, events=[])
+    _, bm, names = fwds[0](x, routing=rb, events=[])
     torch.cuda.synchronize()
     nk = len(names)
     ev = B.HipEvents(nk + 1)
     per = np.zeros(nk)
     reps = max(args.steps, 10)
-    for _ in range(reps):
-        fwd(x, out, events=ev.handles)
+    for i in range(reps):
+        fwds[i % len(fwds)](x, out, events=ev.handles)
         torch.cuda.synchronize()
         per += [ev.elapsed_ms(i, i + 1) for i in range(nk)]
     per /= reps
     kern = {n: float(v) for n, v in zip(names, per)}
-
-    counts = rb["counts"].cpu().numpy()
-    active = int((counts > 0).sum())
-    work = R.layer_work(T, sh.d, sh.d_ff, sh.E, sh.k, sh.act, sh.wdt, active)
     # the roofline is taken for the longer of the two expert GEMMs (the
     # layer's dominant kernels by design; the others have no fixed roofline)
     dom = max((n for n in kern if n in ("gate_up", "down")), key=kern.get)
@@ -115,17 +140,21 @@ def main():
     # other batch sizes of the same layer (same process, same weights)
     sweep = {}
     if not args.no_sweep:
+        nrep_main = len(fwds)
+        del fwds
         for t2 in sh.tokens:
             if t2 == T:
                 continue
-            f2 = B.Forward(layer.w_router, make_bias(sh, sh.zipf_for(t2), dev), layer.w_gate_up,
-                           layer.w_down, sh.k, layer.scale_gate_up, layer.scale_down)
-            fwd_saved = fwd
-            fwd = f2
             x2 = make_tokens(sh, t2, dev)
-            m2, _ = timed(x2, max(args.steps // 2, 5), 3)
-            fwd = fwd_saved
-            sweep[str(t2)] = {"ms": m2, "tokens_per_s": t2 / (m2 * 1e-3)}
+            f2, _, _, _ = guarded_forwards(B, R, layer, make_bias(sh, sh.zipf_for(t2), dev), sh,
+                                           x2, t2)
+            m2, _ = timed(f2, x2, max(args.steps // 2, 5), 3)
+            sweep[str(t2)] = {"ms": m2, "tokens_per_s": t2 / (m2 * 1e-3),
+                              "weight_replicas": len(f2)}
+            del f2
+            torch.cuda.empty_cache()
+    else:
+        nrep_main = len(fwds)
 
     line = {
         "metric": "MoE layer tokens/s; decode HBM GB/s, prefill MFMA TFLOP/s as % of peak",
@@ -144,6 +173,9 @@ def main():
                                f"d={sh.d} d_ff={sh.d_ff} {sh.act} x / {sh.wdt} experts, T={T}",
                    "tokens": T, "E": sh.E, "k": sh.k, "d": sh.d, "d_ff": sh.d_ff,
                    "active_experts": active, "block_m": bm, "parallelism": "single GPU"},
+        "cache_guard": {"weight_replicas": nrep_main,
+                        "layer_bytes": int(work.bytes_total),
+                        "min_bytes_per_cycle": GUARD_BYTES},
         "layer_hbm_GBps": work.bytes_total / (ms * 1e-3) / 1e9,
         "layer_hbm_frac": work.bytes_total / (ms * 1e-3) / R.HBM_BYTES_PER_S,
         "kernels_ms": kern,
