@@ -32,6 +32,8 @@ def parse():
     ap.add_argument("--tokens", type=int, default=None,
                     help="batch size (default: the largest decode batch of the config)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of HIP graphs that capture one forward each")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="also run a plain device copy of MB megabytes (counter calibration)")
@@ -89,14 +91,28 @@ def main():
 
     def timed(fwds, x, steps, warmup):
         out = torch.empty_like(x)
-        for i in range(warmup):
+        for i in range(max(warmup, len(fwds))):
             fwds[i % len(fwds)](x, out)
         torch.cuda.synchronize()
+        run = [lambda f=f: f(x, out) for f in fwds]
+        if args.graph:
+            # one graph per weight copy, each capturing one whole forward
+            graphs = []
+            for f in fwds:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    f(x, out)
+                graphs.append(g)
+            torch.cuda.synchronize()
+            run = [g.replay for g in graphs]
+            for i in range(warmup):
+                run[i % len(run)]()
+            torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(stream)
         for i in range(steps):
-            fwds[i % len(fwds)](x, out)
+            run[i % len(run)]()
         t1.record(stream)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / steps, out
@@ -173,6 +189,7 @@ def main():
                                f"d={sh.d} d_ff={sh.d_ff} {sh.act} x / {sh.wdt} experts, T={T}",
                    "tokens": T, "E": sh.E, "k": sh.k, "d": sh.d, "d_ff": sh.d_ff,
                    "active_experts": active, "block_m": bm, "parallelism": "single GPU"},
+        "launch": "hip graph replay" if args.graph else "eager",
         "cache_guard": {"weight_replicas": nrep_main,
                         "layer_bytes": int(work.bytes_total),
                         "min_bytes_per_cycle": GUARD_BYTES},
