@@ -35,6 +35,7 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of HIP graphs that capture one forward each")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-qk", action="store_true", help="skip the QK-norm measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="also run a plain device copy of MB megabytes (counter calibration)")
     return ap.parse_args()
@@ -200,6 +201,9 @@ def main():
         "sweep": sweep,
     }
 
+    if not args.no_qk:
+        line["qk_norm"] = qk_norm_bench(B, R, dev, args.steps)
+
     if args.copy_calibration:
         # a plain copy of known size, so hardware byte counters can be scaled
         n = args.copy_calibration * (1 << 20)
@@ -213,6 +217,38 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layer, bias, x, sh)
     print(json.dumps(line), flush=True)
+
+
+def qk_norm_bench(B, roof, dev, steps):
+    """In-place QK-norm of the attention shape of the E=128 top-8 layer's model
+    class (32 query and 4 key heads of 128, bf16) over an 8192-token batch:
+    HBM-bound, algorithmic bytes = q and k read once and written once (+ the
+    two weight vectors).  Launches cycle through copies of q and k so that one
+    cycle moves >= 1 GiB (Infinity-Cache guard)."""
+    import torch
+    from workloads.qk import make_qk
+    T, nq, nk, hd = 8192, 32, 4, 128
+    nbytes = 2 * T * (nq + nk) * hd * 2 + 2 * hd * 2
+    copies = max(1, min(MAX_REPLICAS, -(-GUARD_BYTES // nbytes)))
+    sets = [make_qk(T, nq, nk, hd, "bf16", seed=i, device=dev) for i in range(copies)]
+    for i in range(max(3, copies)):
+        q, k, wq, wk = sets[i % copies]
+        B.qk_norm(q, k, wq, wk, eps=1e-6)
+    torch.cuda.synchronize()
+    n = max(steps, 20) * copies
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(n):
+        q, k, wq, wk = sets[i % copies]
+        B.qk_norm(q, k, wq, wk, eps=1e-6)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / n
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": f"QK-norm in place, bf16, T={T}, {nq} q + {nk} k heads of {hd}",
+            "us_per_launch": us, "algorithmic_bytes_per_launch": nbytes, "GB/s": gbs,
+            "frac_of_hbm_peak": gbs * 1e9 / roof.HBM_BYTES_PER_S, "cache_guard_copies": copies}
 
 
 def measured_traffic(kernel, sh, T):

@@ -198,6 +198,31 @@ int moe_forward_traced(const moe_layer* layer, const void* x, int T, void* out,
                        void* workspace, size_t* workspace_bytes,
                        moe_routing_out* routing, moe_trace* trace, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * moe_qk_norm — per-head RMS normalisation of query and key heads (QK-norm),
+ * in place.  "CuTeDSL at Perplexity", section on the RMS-norm kernel
+ * specialised for small dimensions: for every token t and every head of q
+ * (then of k), with x the head's head_dim values and w the tensor's weight,
+ *   x <- (w + weight_bias) * x * rsqrt(sum(x * x) / head_dim + eps),
+ * rounded once to the element type.  (The section's one-line formula omits
+ * the reciprocal square root its kernel listing applies; the listing is
+ * followed.)
+ *
+ *   q         [T, n_q_heads, head_dim]  dtype, read and overwritten
+ *   k         [T, n_k_heads, head_dim]  dtype, read and overwritten
+ *   q_weight  [head_dim] dtype, shared by all q heads
+ *   k_weight  [head_dim] dtype, shared by all k heads
+ *   dtype     MOE_BF16 or MOE_F32
+ * Sums, the root and the weighting run in fp32.  q/q_weight may be NULL when
+ * n_q_heads == 0, k/k_weight when n_k_heads == 0; q and k must not overlap.
+ * Limits: head_dim in {64, 128, 256} (else MOE_ERR_UNSUPPORTED), T >= 0,
+ * head counts >= 0, T * (n_q_heads + n_k_heads) < 2^31, eps >= 0 and finite,
+ * weight_bias finite (else MOE_ERR_INVALID).  No workspace.
+ * ------------------------------------------------------------------------- */
+int moe_qk_norm(void* q, void* k, const void* q_weight, const void* k_weight, int T,
+                int n_q_heads, int n_k_heads, int head_dim, int dtype, float weight_bias,
+                float eps, void* stream);
+
 /* Static description of a status code (host). */
 const char* moe_status_string(int status);
 

@@ -18,7 +18,7 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_BLOCK_M_MAX = 256
 
 EXPORTED = ["moe_align_capacity", "moe_route", "moe_align", "moe_forward", "moe_forward_traced",
-            "moe_status_string", "moe_abi_version"]
+            "moe_qk_norm", "moe_status_string", "moe_abi_version"]
 
 _c = ctypes
 _vp = _c.c_void_p
@@ -76,6 +76,9 @@ def load():
     lib.moe_forward_traced.argtypes = [_c.POINTER(MoeLayer), _vp, _c.c_int, _vp, _vp,
                                        _c.POINTER(_c.c_size_t), _c.POINTER(MoeRoutingOut),
                                        _c.POINTER(MoeTrace), _vp]
+    lib.moe_qk_norm.restype = _c.c_int
+    lib.moe_qk_norm.argtypes = [_vp, _vp, _vp, _vp, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                _c.c_int, _c.c_float, _c.c_float, _vp]
     lib.moe_status_string.restype = _c.c_char_p
     lib.moe_status_string.argtypes = [_c.c_int]
     lib.moe_abi_version.restype = _c.c_int
@@ -162,6 +165,26 @@ def align(topk_ids: torch.Tensor, E: int, block_m: int, stream=None):
     ws, nb = _workspace(call, dev)
     _check(call(_ptr(ws), _c.byref(nb)), "moe_align")
     return out
+
+
+def qk_norm(q: Optional[torch.Tensor], k: Optional[torch.Tensor],
+            q_weight: Optional[torch.Tensor], k_weight: Optional[torch.Tensor],
+            weight_bias: float = 0.0, eps: float = 1e-6, stream=None):
+    """In-place QK-norm of q [T, nq, hd] and k [T, nk, hd] (either may be
+    None); weights [hd] in the same dtype.  Returns (q, k)."""
+    ref = q if q is not None else k
+    T, _, hd = ref.shape
+    nq = 0 if q is None else q.shape[1]
+    nk = 0 if k is None else k.shape[1]
+    for t in (q, k, q_weight, k_weight):
+        if t is not None and (t.dtype != ref.dtype or not t.is_contiguous()):
+            raise ValueError("q, k and the weights: one dtype, contiguous")
+    if k is not None and k.shape[0] != T:
+        raise ValueError("q and k: same token count")
+    _check(load().moe_qk_norm(_ptr(q), _ptr(k), _ptr(q_weight), _ptr(k_weight), T, nq, nk, hd,
+                              act_code(ref.dtype), float(weight_bias), float(eps),
+                              _stream(stream)), "moe_qk_norm")
+    return q, k
 
 
 def make_layer_struct(w_router, bias, w_gate_up, w_down, k, scale_gate_up=None, scale_down=None):

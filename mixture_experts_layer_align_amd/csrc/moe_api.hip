@@ -1,6 +1,7 @@
 // C ABI of libmoe: argument validation, workspace layout, launch order.
 // The ABI itself is documented in include/libmoe.h.
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 
 #include "../../include/libmoe.h"
@@ -223,6 +224,24 @@ int64_t moe_align_capacity(int T, int E, int k, int bm) {
   const int64_t n = (int64_t)T * k;
   if (n == 0) return 0;
   return (int64_t)bm * ((n + std::min<int64_t>(E, n) * (bm - 1)) / bm);
+}
+
+int moe_qk_norm(void* q, void* k, const void* q_weight, const void* k_weight, int T,
+                int n_q_heads, int n_k_heads, int head_dim, int dtype, float weight_bias,
+                float eps, void* stream) {
+  if (T < 0 || n_q_heads < 0 || n_k_heads < 0) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return MOE_ERR_UNSUPPORTED;
+  if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(weight_bias)) return MOE_ERR_INVALID;
+  if ((int64_t)T * (n_q_heads + n_k_heads) >= (int64_t(1) << 31)) return MOE_ERR_INVALID;
+  if (T == 0 || n_q_heads + n_k_heads == 0) return MOE_OK;
+  if (n_q_heads > 0 && (q == nullptr || q_weight == nullptr)) return MOE_ERR_INVALID;
+  if (n_k_heads > 0 && (k == nullptr || k_weight == nullptr)) return MOE_ERR_INVALID;
+  const hipError_t e =
+      launch_qk_norm(dtype == MOE_BF16 ? ACT_BF16 : ACT_F32, q, k, q_weight, k_weight, T,
+                     n_q_heads, n_k_heads, head_dim, weight_bias, eps,
+                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
 int moe_route(const void* x, const void* w_router, const float* logit_bias, int T, int d, int E,

@@ -142,4 +142,13 @@ hipError_t launch_combine(int act_dtype, const float* y, int nsplit, int64_t spl
                           const int32_t* inv_pos, const float* w, int T, int k, int d, void* out,
                           hipStream_t st);
 
+// ------------------------------------------------------------ QK-norm
+
+// In-place per-head RMS normalisation of q [T, nq, head_dim] and k [T, nk,
+// head_dim] (weights [head_dim] each, all in the activation dtype);
+// head_dim * element size must be 128, 256 or 512 (bf16: 64/128/256 elements).
+hipError_t launch_qk_norm(int act_dtype, void* q, void* k, const void* wq, const void* wk, int T,
+                          int nq, int nk, int head_dim, float weight_bias, float eps,
+                          hipStream_t st);
+
 }  // namespace moe

@@ -127,3 +127,31 @@ def test_forward_validation_and_workspace_query():
     assert _fwd(_layer(), T=64, ws=ctypes.c_void_p(4096 + 8), nbytes=need)[0] == B.MOE_ERR_WORKSPACE
     # workspace grows with T
     assert _fwd(_layer(), T=4096)[1] > need
+
+
+def _qk(q=1, k=1, wq=1, wk=1, T=4, nq=2, nk=1, hd=128, dt=B.MOE_BF16, bias=0.0, eps=1e-6):
+    vp = ctypes.c_void_p
+    return B.load().moe_qk_norm(vp(q) if q else None, vp(k) if k else None,
+                                vp(wq) if wq else None, vp(wk) if wk else None, T, nq, nk, hd,
+                                dt, bias, eps, None)
+
+
+def test_qk_norm_validation_before_any_launch():
+    assert _qk(hd=96) == B.MOE_ERR_UNSUPPORTED
+    assert _qk(hd=512) == B.MOE_ERR_UNSUPPORTED
+    assert _qk(dt=B.MOE_FP8_E4M3) == B.MOE_ERR_UNSUPPORTED
+    assert _qk(T=-1) == B.MOE_ERR_INVALID
+    assert _qk(nq=-1) == B.MOE_ERR_INVALID
+    assert _qk(eps=-1e-6) == B.MOE_ERR_INVALID
+    assert _qk(eps=float("nan")) == B.MOE_ERR_INVALID
+    assert _qk(eps=float("inf")) == B.MOE_ERR_INVALID
+    assert _qk(bias=float("inf")) == B.MOE_ERR_INVALID
+    assert _qk(q=0) == B.MOE_ERR_INVALID
+    assert _qk(wk=0) == B.MOE_ERR_INVALID
+    assert _qk(T=1 << 30, nq=2, nk=1) == B.MOE_ERR_INVALID
+
+
+def test_qk_norm_empty_work_enqueues_nothing():
+    # no heads or no tokens: OK without touching the (absent) tensors or a GPU
+    assert _qk(q=0, k=0, wq=0, wk=0, T=0) == B.MOE_OK
+    assert _qk(q=0, k=0, wq=0, wk=0, nq=0, nk=0) == B.MOE_OK
