@@ -35,7 +35,13 @@ Readings where the sources are silent (each one is listed in the design doc):
   R5 within an expert, entries are in ascending (token, slot) order;
   R6 gate columns come first in the concatenated weight, then up columns;
   R7 SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z));
-  R8 fp8 expert weight = decode(code) * scale[e, n] per output column.
+  R8 fp8 expert weight = decode(code) * scale[e, n] per output column;
+  R13 MXFP4 expert weight = e2m1(code) * e8m0(scale) of its 32-element block
+     along K, codes packed two per byte along K (low nibble = even k).
+
+The microscaling formats follow the CuTeDSL post's quantisation remark
+(MXFP8/MXFP4 reduce an absolute maximum over 32 elements) with the element
+and scale encodings of the OCP MX formats (E2M1 elements, E8M0 scales).
 """
 import math
 from typing import Callable, Dict, Optional, Tuple
@@ -79,6 +85,51 @@ def decode_e4m3fn(bits: np.ndarray) -> np.ndarray:
     format definition above, looked up per element."""
     table = _e4m3fn_value(np.arange(256))
     return table[np.asarray(bits).astype(np.uint8)]
+
+
+def _e2m1_value(c: np.ndarray) -> np.ndarray:
+    """OCP MX 4-bit float E2M1: 1 sign bit, 2 exponent bits with bias 1, 1
+    mantissa bit, no infinities or NaN; exponent field 0 encodes subnormals
+    m * 0.5; normals are (1 + m/2) * 2^(e-1), so the magnitudes of codes 0..7
+    are 0, 0.5, 1, 1.5, 2, 3, 4, 6."""
+    c = np.asarray(c).astype(np.int64)
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = (c & 0x1).astype(np.float64)
+    normal = (1.0 + m / 2.0) * np.exp2(e.astype(np.float64) - 1.0)
+    return sign * np.where(e == 0, m * 0.5, normal)
+
+
+def decode_e2m1(codes: np.ndarray) -> np.ndarray:
+    """Decode E2M1 codes (one per element, values 0..15) by the table of the
+    16 values the definition above gives."""
+    table = _e2m1_value(np.arange(16))
+    return table[np.asarray(codes).astype(np.uint8) & 0xF]
+
+
+def decode_e8m0(bits: np.ndarray) -> np.ndarray:
+    """OCP MX shared scale E8M0: an unsigned biased exponent, value 2^(e-127);
+    e = 255 is NaN."""
+    e = np.asarray(bits).astype(np.int64)
+    return np.where(e == 255, np.nan, np.exp2(e.astype(np.float64) - 127.0))
+
+
+MX_BLOCK = 32
+
+
+def decode_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """An MXFP4 matrix W[K, N] from its storage (reading R13): E2M1 codes two per
+    byte along K, packed[k/2, n] holding code(k) in the low nibble for even k
+    and code(k+1) in the high nibble; scales[k/32, n] the E8M0 scale shared by
+    the block of 32 consecutive k of column n.  W[k, n] = e2m1(code) * scale."""
+    packed = np.asarray(packed).astype(np.uint8)
+    K2, N = packed.shape
+    codes = np.empty((2 * K2, N), np.uint8)
+    codes[0::2] = packed & 0xF
+    codes[1::2] = packed >> 4
+    vals = decode_e2m1(codes)
+    sc = decode_e8m0(scales)
+    return vals * np.repeat(sc, MX_BLOCK, axis=0)[: 2 * K2]
 
 
 def decode(raw: np.ndarray, fmt: str) -> np.ndarray:
@@ -214,10 +265,17 @@ def expert_weights_from_raw(w_gate_up, w_down, fmt: str, scale_gate_up=None,
                             scale_down=None) -> ExpertFn:
     """Expert e's float64 (W_gate[d, d_ff], W_up[d, d_ff], W_down[d_ff, d]) from
     the stored arrays.  `w_gate_up[e]` is [d, 2*d_ff], gate columns first
-    (reading R6); fp8 weights are decode(code) * scale per output column (R8).
+    (reading R6); fp8 weights are decode(code) * scale per output column (R8);
+    MXFP4 weights are E2M1 codes times the E8M0 scale of their 32-element block
+    along K (R13).
     The arrays only need `[e]` indexing returning NumPy arrays, so experts can be
     fetched one at a time."""
     def fn(e: int):
+        if fmt == "mxfp4":
+            gu = decode_mxfp4(np.asarray(w_gate_up[e]), np.asarray(scale_gate_up[e]))
+            dn = decode_mxfp4(np.asarray(w_down[e]), np.asarray(scale_down[e]))
+            dff = gu.shape[1] // 2
+            return gu[:, :dff], gu[:, dff:], dn
         gu = decode(np.asarray(w_gate_up[e]), fmt)
         dn = decode(np.asarray(w_down[e]), fmt)
         if fmt == "fp8":

@@ -20,7 +20,7 @@ class LayerShape:
     d: int
     d_ff: int
     act: str            # "f32" | "bf16"   (x, out, router weight)
-    wdt: str            # "f32" | "bf16" | "fp8"  (expert weights)
+    wdt: str            # "f32" | "bf16" | "fp8" | "mxfp4"  (expert weights)
     tokens: List[int] = field(default_factory=list)
     # Zipf exponent of the router-logit bias per token count (None: no bias)
     zipf: Dict[int, Optional[float]] = field(default_factory=dict)
@@ -47,6 +47,10 @@ CONFIGS = {
     4: LayerShape(4, "large-fp8-zipf1.2", E=256, k=8, d=7168, d_ff=2048, act="bf16",
                   wdt="fp8", tokens=[1, 16, 128, 16384], zipf=_z([1, 16, 128, 16384], 1.2),
                   seed=4),
+    # not one of the five benchmark layers: the layer of config 4 with MXFP4
+    # experts (the microscaling variant), decode batches only
+    5: LayerShape(5, "large-mxfp4-zipf1.2", E=256, k=8, d=7168, d_ff=2048, act="bf16",
+                  wdt="mxfp4", tokens=[1, 16, 128], zipf=_z([1, 16, 128], 1.2), seed=5),
 }
 
 

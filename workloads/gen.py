@@ -13,6 +13,8 @@ the oracle):
   * fp8 experts: per expert and per output column, scale = max_k |w[k, n]| / 448
     (the OCP e4m3fn maximum), code = e4m3fn(w / scale) by torch's RNE cast; gate
     and up columns are scaled separately.
+  * MXFP4 experts: per block of 32 consecutive k of one output column, an
+    E8M0 exponent floor(log2(max|w|)) - 2 and E2M1 codes (quantize_mxfp4).
   * Zipf router skew: bias[e] = -s * ln(rank[e]) with rank a seeded permutation
     of 1..E, which multiplies each expert's softmax mass by rank^-s.
 
@@ -62,6 +64,36 @@ def quantize_e4m3fn_per_column(w: torch.Tensor):
     return q, scale.to(torch.float32)
 
 
+MX_BLOCK = 32
+# E2M1 magnitudes of codes 0..7
+_E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def quantize_mxfp4(w: torch.Tensor):
+    """w: [K, N] fp32 (K a multiple of 32) -> (packed [K/2, N] uint8, scales
+    [K/32, N] uint8).  Per block of 32 consecutive k of one column: shared
+    exponent floor(log2(max|w|)) - 2 (E2M1's largest magnitude is 1.5 * 2^2),
+    stored biased by 127 (E8M0); each element divided by 2^exponent and rounded
+    to the nearest E2M1 magnitude (ties to the even code, beyond 6 clamped to
+    6); codes two per byte along K, even k in the low nibble.  An all-zero
+    block gets exponent 0 and zero codes."""
+    K, N = w.shape
+    blk = w.reshape(K // MX_BLOCK, MX_BLOCK, N)
+    amax = blk.abs().amax(dim=1)
+    ex = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, 1.0))) - 2.0,
+                     torch.zeros_like(amax)).clamp_(-127.0, 127.0)
+    x = (blk / torch.exp2(ex)[:, None, :]).reshape(K, N)
+    grid = torch.tensor(_E2M1_GRID, dtype=torch.float32, device=w.device)
+    mag = x.abs().clamp(max=6.0)
+    dist = (mag[..., None] - grid).abs()
+    # exact ties go to the even code (mantissa bit 0)
+    dist = dist + (torch.arange(8, device=w.device) & 1).to(torch.float32) * 1e-12
+    code = dist.argmin(dim=-1).to(torch.uint8)
+    code = torch.where((x < 0) & (code > 0), code | 8, code)
+    packed = (code[0::2] | (code[1::2] << 4)).to(torch.uint8)
+    return packed.contiguous(), (ex + 127.0).to(torch.uint8).contiguous()
+
+
 @dataclass
 class Layer:
     shape: LayerShape
@@ -101,7 +133,12 @@ def make_layer(shape: LayerShape, T: Optional[int] = None, device="cpu",
     E, d, dff = shape.E, shape.d, shape.d_ff
     s = shape.seed
     w_router = make_router(shape, device)
-    if shape.wdt == "fp8":
+    if shape.wdt == "mxfp4":
+        wgu = torch.empty((E, d // 2, 2 * dff), dtype=torch.uint8, device=device)
+        wdn = torch.empty((E, dff // 2, d), dtype=torch.uint8, device=device)
+        sgu = torch.empty((E, d // MX_BLOCK, 2 * dff), dtype=torch.uint8, device=device)
+        sdn = torch.empty((E, dff // MX_BLOCK, d), dtype=torch.uint8, device=device)
+    elif shape.wdt == "fp8":
         wgu = torch.empty((E, d, 2 * dff), dtype=torch.float8_e4m3fn, device=device)
         wdn = torch.empty((E, dff, d), dtype=torch.float8_e4m3fn, device=device)
         sgu = torch.empty((E, 2 * dff), dtype=torch.float32, device=device)
@@ -115,7 +152,10 @@ def make_layer(shape: LayerShape, T: Optional[int] = None, device="cpu",
         wg = _normal((d, dff), d ** -0.5, device, s, TENSOR_WG, e)
         wu = _normal((d, dff), d ** -0.5, device, s, TENSOR_WU, e)
         wd = _normal((dff, d), dff ** -0.5, device, s, TENSOR_WD, e)
-        if shape.wdt == "fp8":
+        if shape.wdt == "mxfp4":
+            wgu[e], sgu[e] = quantize_mxfp4(torch.cat([wg, wu], dim=1))
+            wdn[e], sdn[e] = quantize_mxfp4(wd)
+        elif shape.wdt == "fp8":
             qg, sg = quantize_e4m3fn_per_column(wg)
             qu, su = quantize_e4m3fn_per_column(wu)
             qd, sd = quantize_e4m3fn_per_column(wd)
