@@ -184,7 +184,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if sh.wdt == "bf16" else ("f32" if sh.wdt == "f32" else "bf16-act/fp8-weight"),
+        "dtype": {"bf16": "bf16", "f32": "f32", "fp8": "bf16-act/fp8-weight",
+                  "mxfp4": "bf16-act/mxfp4-weight"}[sh.wdt],
         "data": "synthetic",
         "config": {"workload": f"fused MoE layer forward, {sh.name}: E={sh.E} top-{sh.k} "
                                f"d={sh.d} d_ff={sh.d_ff} {sh.act} x / {sh.wdt} experts, T={T}",

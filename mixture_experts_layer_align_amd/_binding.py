@@ -14,7 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = 0, -1, -2, -3, -4
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
 MOE_BLOCK_M_MAX = 256
 
 EXPORTED = ["moe_align_capacity", "moe_route", "moe_align", "moe_forward", "moe_forward_traced",
@@ -106,7 +106,8 @@ def _check(rc: int, what: str):
 
 
 _ACT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
-_WDT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.float8_e4m3fn: MOE_FP8_E4M3}
+_WDT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.float8_e4m3fn: MOE_FP8_E4M3,
+        torch.uint8: MOE_MXFP4}  # uint8 expert weights: packed MXFP4 codes
 
 
 def act_code(dt: torch.dtype) -> int:
@@ -189,6 +190,8 @@ def qk_norm(q: Optional[torch.Tensor], k: Optional[torch.Tensor],
 
 def make_layer_struct(w_router, bias, w_gate_up, w_down, k, scale_gate_up=None, scale_down=None):
     E, d, two_dff = w_gate_up.shape
+    if w_gate_up.dtype == torch.uint8:
+        d *= 2  # MXFP4: two codes per byte along K
     L = MoeLayer()
     L.d, L.d_ff, L.E, L.k = d, two_dff // 2, E, k
     L.act_dtype = _ACT[w_router.dtype]

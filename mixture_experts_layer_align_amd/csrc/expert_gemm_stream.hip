@@ -75,6 +75,17 @@ struct DTr<W_FP8> {
   static constexpr int KSTEP = 32;
   static constexpr int ESIZE = 1;
 };
+// MXFP4: one 16-byte load holds two k-rows (a packed byte per column) of 16
+// columns, so 4 loads cover the lane's 8 k-rows; converted, byte c of the 4
+// loads is directly the 8 consecutive-k bf16 operand of column c (no
+// transpose), scaled by that column's E8M0 block scale during the conversion.
+template <>
+struct DTr<W_FP4> {
+  static constexpr int CPL = 16;
+  static constexpr int RPL = 4;
+  static constexpr int KSTEP = 32;  // = the MX block: one scale per column per k-step
+  static constexpr int ESIZE = 1;   // (bytes per packed row pair and column)
+};
 template <>
 struct DTr<W_F32> {
   static constexpr int CPL = 4;
@@ -89,7 +100,7 @@ struct DTr<W_F32> {
 // larger LDS footprint keeps two workgroups per compute unit.
 template <int WT>
 constexpr int stages_of() {
-  return WT == W_BF16 ? 2 : 4;
+  return WT == W_BF16 ? 2 : 4;  // fp8 and MXFP4: four
 }
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
@@ -97,6 +108,21 @@ constexpr int stages_of() {
 // left alone.
 constexpr int vmcnt_imm(int n) {
   return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14);
+}
+
+// Two E2M1 codes (byte `sel` of src: low nibble -> low half) to two bf16,
+// times `scale` (exact for the power-of-two MX scales).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t src, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scale, SEL));
+}
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t src, float scale, int sel) {
+  switch (sel) {  // sel is a constant after unrolling
+    case 0: return fp4x2_to_bf16x2<0>(src, scale);
+    case 1: return fp4x2_to_bf16x2<1>(src, scale);
+    case 2: return fp4x2_to_bf16x2<2>(src, scale);
+    default: return fp4x2_to_bf16x2<3>(src, scale);
+  }
 }
 
 __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
@@ -117,7 +143,9 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
   constexpr int ASZ = (ACT == ACT_BF16) ? 2 : 4;
   constexpr int XK = (ACT == ACT_BF16) ? 8 : 4;  // k-values per lane per token fragment
   constexpr int S = stages_of<WT>();
-  constexpr int PER = RPL + 2;    // vector-memory ops per stage: weight rows + 2 token loads
+  constexpr bool MX = WT == W_FP4;
+  // vector-memory ops per stage: weight rows + 2 token loads (+ the MX scales)
+  constexpr int PER = RPL + 2 + (MX ? 1 : 0);
   static_assert((S - 1) * PER <= 63, "vmcnt field");
 
   const int lane = threadIdx.x & 63;
@@ -158,12 +186,21 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
   }
   // the second slab of the last down tile may lie past the output width
   const bool active = (EPI != EPI_STORE) || (nt * 2 * SW + slab * SW < p.n_out);
+  // bytes between consecutive weight rows (MX: packed row pairs) and per k-step
   const int64_t wrow_bytes = p.w_ld * Tr::ESIZE;
+  const int64_t kstep_bytes = (MX ? KSTEP / 2 : KSTEP) * wrow_bytes;
   const int kb = split * p.kchunk;
   const int ke = min(p.K, kb + p.kchunk);
   const int nsteps = (ke - kb) / KSTEP;
-  const char* wbase = reinterpret_cast<const char*>(p.w) + (int64_t)e * p.w_estride * Tr::ESIZE +
-                      (int64_t)(kb + lg * RPL) * wrow_bytes + (int64_t)wcol * Tr::ESIZE;
+  const char* wbase =
+      MX ? reinterpret_cast<const char*>(p.w) + (int64_t)e * (p.w_estride / 2) +
+               (int64_t)(kb / 2 + lg * RPL) * wrow_bytes + wcol
+         : reinterpret_cast<const char*>(p.w) + (int64_t)e * p.w_estride * Tr::ESIZE +
+               (int64_t)(kb + lg * RPL) * wrow_bytes + (int64_t)wcol * Tr::ESIZE;
+  // MX: the E8M0 scales of the lane's 16 columns for the k-step's block
+  const char* sbase = MX ? reinterpret_cast<const char*>(p.scale) + (int64_t)e * p.scale_estride +
+                               (int64_t)(kb / KSTEP) * p.w_ld + wcol
+                         : nullptr;
   u32x4* ring = lds + slab * S * RPL * WAVE;
 
   f32x4 acc[2][CPL];
@@ -174,15 +211,17 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
 
   if (active && nsteps > 0) {
     u32x4 xb[S][2];
+    u32x4 mxs[MX ? S : 1];
     // stage s <- k-step `step` (clamped: steps past the end reload the last)
     auto issue = [&](int s, int step) {
       const int sc = min(step, nsteps - 1);
-      const char* src = wbase + (int64_t)sc * KSTEP * wrow_bytes;
+      const char* src = wbase + (int64_t)sc * kstep_bytes;
 #pragma unroll
       for (int j = 0; j < RPL; ++j) dma16(src + j * wrow_bytes, ring + (s * RPL + j) * WAVE);
       const int64_t kk = (int64_t)(kb + sc * KSTEP + XK * lg) * ASZ;
       xb[s][0] = ld16(arow[0] + kk);
       xb[s][1] = ld16(arow[1] + kk);
+      if constexpr (MX) mxs[s] = ld16(sbase + (int64_t)sc * p.w_ld);
     };
     auto compute = [&](int s) {
       u32x4 raw[RPL];
@@ -207,6 +246,18 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
         for (int c = 0; c < 8; ++c) {
           acc[0][c] = mfma_bf16_16x16x32(frag[c], x0, acc[0][c]);
           if (use_q1) acc[1][c] = mfma_bf16_16x16x32(frag[c], x1, acc[1][c]);
+        }
+      } else if constexpr (WT == W_FP4) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          // E8M0 byte e -> the fp32 2^(e-127) (exponent field e, zero mantissa)
+          const float scl = __uint_as_float(((mxs[s][c >> 2] >> (8 * (c & 3))) & 0xFFu) << 23);
+          u32x4 frag;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            frag[j] = fp4x2_to_bf16x2(raw[j][c >> 2], scl, c & 3);
+          acc[0][c] = mfma_bf16_16x16x32(frag, x0, acc[0][c]);
+          if (use_q1) acc[1][c] = mfma_bf16_16x16x32(frag, x1, acc[1][c]);
         }
       } else {
 #pragma unroll
@@ -400,8 +451,10 @@ hipError_t launch_splitk_silu(int act, const float* part, int nsplit, int64_t sp
 }
 
 int stream_tile_cols(int w_dtype, int epi) {
-  const int sw = 16 * (w_dtype == W_F32 ? DTr<W_F32>::CPL
-                                         : (w_dtype == W_FP8 ? DTr<W_FP8>::CPL : DTr<W_BF16>::CPL));
+  const int sw = 16 * (w_dtype == W_F32   ? DTr<W_F32>::CPL
+                       : w_dtype == W_FP8 ? DTr<W_FP8>::CPL
+                       : w_dtype == W_FP4 ? DTr<W_FP4>::CPL
+                                          : DTr<W_BF16>::CPL);
   return epi == EPI_SILU_MUL ? sw : 2 * sw;
 }
 
@@ -428,6 +481,8 @@ hipError_t launch_stream_gemm(int act, int wdt, int epi, const StreamGemmArgs& a
   MOE_CASE(ACT_BF16, W_BF16, EPI_STORE)
   MOE_CASE(ACT_BF16, W_FP8, EPI_SILU_MUL)
   MOE_CASE(ACT_BF16, W_FP8, EPI_STORE)
+  MOE_CASE(ACT_BF16, W_FP4, EPI_SILU_MUL)
+  MOE_CASE(ACT_BF16, W_FP4, EPI_STORE)
 #undef MOE_CASE
   return hipErrorInvalidValue;
 }

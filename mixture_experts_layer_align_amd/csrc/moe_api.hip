@@ -48,7 +48,9 @@ struct Carve {
 };
 
 int act_code(int dt) { return dt == MOE_BF16 ? ACT_BF16 : ACT_F32; }
-int w_code(int dt) { return dt == MOE_FP8_E4M3 ? W_FP8 : (dt == MOE_BF16 ? W_BF16 : W_F32); }
+int w_code(int dt) {
+  return dt == MOE_FP8_E4M3 ? W_FP8 : dt == MOE_MXFP4 ? W_FP4 : dt == MOE_BF16 ? W_BF16 : W_F32;
+}
 int act_bytes(int dt) { return dt == MOE_BF16 ? 2 : 4; }
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -206,7 +208,7 @@ int device_cus() {
 
 extern "C" {
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
 
 const char* moe_status_string(int s) {
   switch (s) {
@@ -308,18 +310,22 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   if (d % 128 != 0 || dff % 128 != 0) return MOE_ERR_UNSUPPORTED;
   const bool pair_ok = (L->act_dtype == MOE_F32 && L->w_dtype == MOE_F32) ||
                        (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_BF16) ||
-                       (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_FP8_E4M3);
+                       (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_FP8_E4M3) ||
+                       (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_MXFP4);
   if (!pair_ok) return MOE_ERR_UNSUPPORTED;
-  // fp8 expert slabs are 256 columns wide
-  if (L->w_dtype == MOE_FP8_E4M3 && (d % 256 != 0 || dff % 256 != 0)) return MOE_ERR_UNSUPPORTED;
-  if (L->w_dtype == MOE_FP8_E4M3 && (L->scale_gate_up == nullptr || L->scale_down == nullptr))
+  // fp8 and MXFP4 expert slabs are 256 columns wide
+  const bool scaled = L->w_dtype == MOE_FP8_E4M3 || L->w_dtype == MOE_MXFP4;
+  if (scaled && (d % 256 != 0 || dff % 256 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (scaled && (L->scale_gate_up == nullptr || L->scale_down == nullptr))
     return MOE_ERR_INVALID;
+  const bool mx = L->w_dtype == MOE_MXFP4;
 
   const int act = act_code(L->act_dtype);
   const int wdt = w_code(L->w_dtype);
   const int ab = act_bytes(L->act_dtype);
   const int64_t n = (int64_t)T * k;
   // regime: thick blocks go to the MFMA-tiled GEMM when its shapes fit
+  // (MXFP4 weights always take the weight-streaming GEMM)
   const bool tiled = act == ACT_BF16 && (wdt == W_BF16 || wdt == W_FP8) &&
                      n >= (int64_t)TILED_MIN_ROWS * E &&
                      d % TILED_BN == 0 && dff % (TILED_BN / 2) == 0;
@@ -436,8 +442,9 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g.w = L->w_gate_up;
   g.w_ld = 2 * (int64_t)dff;
   g.w_estride = (int64_t)d * 2 * dff;
-  g.scale = L->scale_gate_up;
-  g.scale_estride = 2 * (int64_t)dff;
+  g.scale = static_cast<const float*>(L->scale_gate_up);
+  // fp8: one fp32 per column; MXFP4: one byte per column and 32-row block
+  g.scale_estride = mx ? (int64_t)(d / 32) * 2 * dff : 2 * (int64_t)dff;
   g.K = d;
   g.n_out = dff;
   g.up_off = dff;
@@ -473,8 +480,8 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g2.w = L->w_down;
   g2.w_ld = d;
   g2.w_estride = (int64_t)dff * d;
-  g2.scale = L->scale_down;
-  g2.scale_estride = d;
+  g2.scale = static_cast<const float*>(L->scale_down);
+  g2.scale_estride = mx ? (int64_t)(dff / 32) * d : d;
   g2.K = dff;
   g2.n_out = d;
   g2.n_tiles = dn_tiles;

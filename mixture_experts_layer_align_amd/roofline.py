@@ -51,12 +51,17 @@ def layer_work(T: int, d: int, d_ff: int, E: int, k: int, act: str, wdt: str,
                active: int) -> LayerWork:
     """`active` is the number of distinct experts the routing selected."""
     bx = ELEM_BYTES[act]
-    bw = ELEM_BYTES[wdt]
-    scales_gu = active * 2 * d_ff * 4 if wdt == "fp8" else 0
-    scales_dn = active * d * 4 if wdt == "fp8" else 0
     rows = T * k
-    w_gu = active * matrix_bytes(d, 2 * d_ff, bw) + scales_gu
-    w_dn = active * matrix_bytes(d_ff, d, bw) + scales_dn
+    if wdt == "mxfp4":
+        # half a byte per weight, one E8M0 byte per 32 k of a column
+        w_gu = active * (d * 2 * d_ff // 2 + (d // 32) * 2 * d_ff)
+        w_dn = active * (d_ff * d // 2 + (d_ff // 32) * d)
+    else:
+        bw = ELEM_BYTES[wdt]
+        scales_gu = active * 2 * d_ff * 4 if wdt == "fp8" else 0
+        scales_dn = active * d * 4 if wdt == "fp8" else 0
+        w_gu = active * matrix_bytes(d, 2 * d_ff, bw) + scales_gu
+        w_dn = active * matrix_bytes(d_ff, d, bw) + scales_dn
     # gate|up reads its weights and the tokens once and writes h once;
     # down reads its weights and h once and writes the per-slot outputs once;
     # combine reads those outputs once and writes the layer output once.

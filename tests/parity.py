@@ -28,10 +28,13 @@ def np_bits(t: torch.Tensor) -> np.ndarray:
         return t.view(torch.uint8).cpu().numpy()
     if t.dtype == torch.float32:
         return t.cpu().numpy()
+    if t.dtype == torch.uint8:  # MXFP4 codes / E8M0 scales
+        return t.cpu().numpy()
     raise TypeError(t.dtype)
 
 
-FMT = {torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8", torch.float32: "f32"}
+FMT = {torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8", torch.float32: "f32",
+       torch.uint8: "mxfp4"}
 
 
 def decode(t: torch.Tensor) -> np.ndarray:
@@ -52,9 +55,9 @@ def oracle_layer(layer):
     bias = None if layer.bias is None else layer.bias.detach().cpu().numpy().astype(np.float64)
     fmt = FMT[layer.w_gate_up.dtype]
     sgu = sdn = None
-    if fmt == "fp8":
-        sgu = layer.scale_gate_up.cpu().numpy()
-        sdn = layer.scale_down.cpu().numpy()
+    if fmt in ("fp8", "mxfp4"):
+        sgu = _PerExpert(layer.scale_gate_up) if fmt == "mxfp4" else layer.scale_gate_up.cpu().numpy()
+        sdn = _PerExpert(layer.scale_down) if fmt == "mxfp4" else layer.scale_down.cpu().numpy()
     fn = O.expert_weights_from_raw(_PerExpert(layer.w_gate_up), _PerExpert(layer.w_down), fmt,
                                    sgu, sdn)
     return wr, bias, fn

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = B.load()
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     for s in (B.MOE_OK, B.MOE_ERR_INVALID, B.MOE_ERR_UNSUPPORTED, B.MOE_ERR_WORKSPACE,
               B.MOE_ERR_DEVICE):
         assert len(B.status_string(s)) > 0
@@ -155,3 +155,22 @@ def test_qk_norm_empty_work_enqueues_nothing():
     # no heads or no tokens: OK without touching the (absent) tensors or a GPU
     assert _qk(q=0, k=0, wq=0, wk=0, T=0) == B.MOE_OK
     assert _qk(q=0, k=0, wq=0, wk=0, nq=0, nk=0) == B.MOE_OK
+
+
+def test_mxfp4_layer_validation():
+    # MXFP4 experts need bf16 activations, 256-wide d and d_ff, and both scales
+    Bd = B
+    layer = Bd.MoeLayer()
+    layer.d, layer.d_ff, layer.E, layer.k = 256, 256, 8, 2
+    layer.act_dtype, layer.w_dtype = Bd.MOE_BF16, Bd.MOE_MXFP4
+    layer.w_router = layer.w_gate_up = layer.w_down = 1
+    lib = Bd.load()
+    n = ctypes.c_size_t(0)
+    q = lambda L: lib.moe_forward(ctypes.byref(L), None, 4, None, None, ctypes.byref(n), None, None)
+    assert q(layer) == Bd.MOE_ERR_INVALID          # scales missing
+    layer.scale_gate_up = layer.scale_down = 1
+    assert q(layer) == Bd.MOE_OK and n.value > 0    # workspace query
+    layer.d_ff = 384
+    assert q(layer) == Bd.MOE_ERR_UNSUPPORTED       # not a multiple of 256
+    layer.d_ff, layer.act_dtype = 256, Bd.MOE_F32
+    assert q(layer) == Bd.MOE_ERR_UNSUPPORTED       # fp32 activations

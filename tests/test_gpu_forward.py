@@ -81,6 +81,11 @@ SMALL = [
     (4, 2, 256, 512, "bf16", "fp8", 400, None),
     (16, 4, 512, 256, "bf16", "fp8", 700, 1.0),      # skewed, ragged blocks
     (2, 1, 768, 256, "bf16", "fp8", 600, None),      # 24 k-steps of gate|up
+    # MXFP4 experts (E2M1 codes, an E8M0 scale per 32 k): always the stream GEMM
+    (8, 2, 256, 256, "bf16", "mxfp4", 5, None),
+    (32, 8, 512, 256, "bf16", "mxfp4", 40, 1.2),
+    (4, 2, 256, 512, "bf16", "mxfp4", 300, None),    # many rows per expert
+    (16, 4, 768, 256, "bf16", "mxfp4", 257, 1.0),    # 24 scale blocks along d
 ]
 
 
