@@ -97,10 +97,12 @@ struct DTr<W_F32> {
 // Load-ring stages per wave.  bf16: two — with fewer requests outstanding
 // HBM serves the weight stream faster (more stages measured slower on gfx950).
 // fp8: four — its heavier per-stage math needs the deeper ring, and the
-// larger LDS footprint keeps two workgroups per compute unit.
+// larger LDS footprint keeps two workgroups per compute unit.  MXFP4: eight
+// stages of 4 KB (the same bytes in flight as fp8; with four its waves spent
+// half their time waiting for loads).
 template <int WT>
 constexpr int stages_of() {
-  return WT == W_BF16 ? 2 : 4;  // fp8 and MXFP4: four
+  return WT == W_BF16 ? 2 : WT == W_FP4 ? 8 : 4;
 }
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
