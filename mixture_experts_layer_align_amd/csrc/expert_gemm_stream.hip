@@ -51,6 +51,7 @@
 // MFMA (activations stay bf16).  fp32 weights: 4 columns per lane, no
 // transpose, v_mfma_f32_16x16x4_f32.
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_common.h"
 #include "moe_internal.h"
@@ -225,7 +226,9 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
       xb[s][1] = ld16(arow[1] + kk);
       if constexpr (MX) mxs[s] = ld16(sbase + (int64_t)sc * p.w_ld);
     };
-    auto compute = [&](int s) {
+    // q1: the block's second 16-row group holds routed rows — a runtime bool
+    // (a branch per MFMA) or, for MXFP4, std::true_type/false_type (folded)
+    auto compute = [&](int s, auto q1) {
       u32x4 raw[RPL];
 #pragma unroll
       for (int j = 0; j < RPL; ++j) raw[j] = ring[(s * RPL + j) * WAVE + lane];
@@ -239,7 +242,7 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
           for (int c = 0; c < CPL; ++c) {
             const float a = __uint_as_float(raw[ss][c]);
             acc[0][c] = mfma_f32_16x16x4(a, __uint_as_float(x0[ss]), acc[0][c]);
-            if (use_q1) acc[1][c] = mfma_f32_16x16x4(a, __uint_as_float(x1[ss]), acc[1][c]);
+            if (q1) acc[1][c] = mfma_f32_16x16x4(a, __uint_as_float(x1[ss]), acc[1][c]);
           }
       } else if constexpr (WT == W_BF16) {
         u32x4 frag[8];
@@ -247,7 +250,7 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           acc[0][c] = mfma_bf16_16x16x32(frag[c], x0, acc[0][c]);
-          if (use_q1) acc[1][c] = mfma_bf16_16x16x32(frag[c], x1, acc[1][c]);
+          if (q1) acc[1][c] = mfma_bf16_16x16x32(frag[c], x1, acc[1][c]);
         }
       } else if constexpr (WT == W_FP4) {
 #pragma unroll
@@ -259,7 +262,7 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
           for (int j = 0; j < 4; ++j)
             frag[j] = fp4x2_to_bf16x2(raw[j][c >> 2], scl, c & 3);
           acc[0][c] = mfma_bf16_16x16x32(frag, x0, acc[0][c]);
-          if (use_q1) acc[1][c] = mfma_bf16_16x16x32(frag, x1, acc[1][c]);
+          if (q1) acc[1][c] = mfma_bf16_16x16x32(frag, x1, acc[1][c]);
         }
       } else {
 #pragma unroll
@@ -272,24 +275,36 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
             acc[0][8 * half + c] = mfma_bf16_16x16x32(frag[c], x0, acc[0][8 * half + c]);
-            if (use_q1) acc[1][8 * half + c] = mfma_bf16_16x16x32(frag[c], x1, acc[1][8 * half + c]);
+            if (q1) acc[1][8 * half + c] = mfma_bf16_16x16x32(frag[c], x1, acc[1][8 * half + c]);
           }
         }
       }
     };
 #pragma unroll
     for (int s = 0; s < S; ++s) issue(s, s);
-    for (int it = 0; it < nsteps; it += S) {
+    auto main_loop = [&](auto q1_c) {
+      for (int it = 0; it < nsteps; it += S) {
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        // stage s complete: only the S-1 later stages may still be in flight
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * PER));
-        __builtin_amdgcn_sched_barrier(0);
-        if (it + s < nsteps) compute(s);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(s, it + s + S);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int s = 0; s < S; ++s) {
+          // stage s complete: only the S-1 later stages may still be in flight
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * PER));
+          __builtin_amdgcn_sched_barrier(0);
+          if (it + s < nsteps) compute(s, q1_c);
+          __builtin_amdgcn_sched_barrier(0);
+          issue(s, it + s + S);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+    };
+    // MXFP4 gains from one loop per case (its many conversions leave no issue
+    // slots for the branches); bf16 measured slower with two loop copies
+    if constexpr (WT == W_FP4) {
+      if (use_q1)
+        main_loop(std::true_type{});
+      else
+        main_loop(std::false_type{});
+    } else {
+      main_loop(use_q1);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
