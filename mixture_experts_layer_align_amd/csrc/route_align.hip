@@ -350,8 +350,8 @@ __global__ __launch_bounds__(AL_THREADS) void k_align_single(const AlignArgs a) 
 }
 
 // ================================================================ small batch
-// Routing and alignment of a few tokens (T <= AL_WAVES) in one launch: wave t
-// routes token t exactly as k_topk does (same plane order, same selection
+// Routing and alignment of a few tokens in one launch: wave w routes tokens
+// w, w + 16, ... exactly as k_topk does (same plane order, same selection
 // and weight arithmetic, so the same bits), keeping its k <= 64 selections in
 // lane registers; the ids also go to LDS, from where the workgroup aligns
 // them as k_align_single does.  One launch and one global round trip fewer.
@@ -402,8 +402,7 @@ __global__ __launch_bounds__(AL_THREADS) void k_route_align_small(
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int E = a.E, k = a.k;
-  if (wave < a.T) {
-    const int t = wave;
+  for (int t = wave; t < a.T; t += AL_WAVES) {
     float acc[4][V];
     plane_sums_all<V, ROUTER_MAX_SPLIT>(partial + (int64_t)t * E, nsplit, split_stride, E, lane,
                                         acc);
