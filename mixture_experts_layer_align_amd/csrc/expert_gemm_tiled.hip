@@ -4,15 +4,20 @@
 // ("CuTeDSL at Perplexity", prefill/decode section: prefill GEMMs are
 // compute-bound), so the kernel is a classic tiled GEMM on the MFMA units:
 //
-//   * a workgroup (4 waves, 2 x 2) computes a BM-row block of one expert (the
-//     aligned, padded slot list; BM = 128 or 256) against 256 weight columns —
-//     for gate|up the 128 gate columns of its h-tile and the matching 128 up
-//     columns, so SiLU(g)*u is applied to the fp32 accumulators in registers
-//     before the single store of h ("La fusion de noyaux", section 4.2, GEMM +
-//     epilogue; the concatenated d x 2*d_ff gate|up); each wave owns a
-//     (BM/2) x 128 sub-tile;
+//   * a workgroup (4 waves) computes one tile of one expert's aligned, padded
+//     slot list: a full tile is 256 rows against 256 weight columns (waves
+//     2 x 2), a half tile 128 rows against 512 columns (waves 1 x 4) — the
+//     alignment pads each expert to 128 rows and cuts its slots into
+//     256-row rows plus, where 128 remain, one 128-row row, so an expert's
+//     last rows cost half the padding a 256-row tile would; either way each
+//     wave owns 128 rows x 128 columns.  For gate|up, 256 weight columns are
+//     the 128 gate columns of an h-tile and the matching 128 up columns, so
+//     SiLU(g)*u is applied to the fp32 accumulators in registers before the
+//     single store of h ("La fusion de noyaux", section 4.2, GEMM +
+//     epilogue; the concatenated d x 2*d_ff gate|up);
 //   * K advances 32 at a time (one v_mfma_f32_16x16x32_bf16 deep) through a
-//     ring of LDS stages (4 for BM = 256, 6 for BM = 128) filled by direct
+//     ring of LDS stages (4 for bf16 weights, 6 for fp8; a stage holds the
+//     larger shape's tiles) filled by direct
 //     loads (global_load_lds_dwordx4): the token tile is gathered row by row
 //     from x by slot (the permuted activations are never materialised), the
 //     weight tile is copied untransposed ([K, N], N contiguous, the B[K,N] of
@@ -53,12 +58,11 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = 256;   // rows per block
-constexpr int TBN = 256;  // weight columns per tile
+constexpr int TBN = 256;  // weight columns per weight sub-tile
 constexpr int TBK = 32;   // k per step and per LDS stage
 constexpr int GROUP_M = 8;
 constexpr int NXCD = 8;   // accelerator complex dies; workgroup i runs on die i % 8
-constexpr int MI = BM / 32;       // 16-row A fragments per wave (BM/2 rows)
+constexpr int MI = 8;             // 16-row A fragments per wave (128 rows)
 constexpr int NMFMA = MI * 8;     // MFMAs per wave per step
 
 // per weight type: element bytes, 16-byte chunks per weight-tile row, LDS
@@ -73,19 +77,33 @@ template <>
 struct TCfg<W_FP8> {
   static constexpr int ESZ = 1, CHUNKS = 16, RD_PER_FRAG = 1, STAGES = 6;
 };
-template <int WT>
+// Tile shapes.  Full: 256 rows x 256 columns, waves 2 x 2.  Half: 128 rows
+// x 512 columns (two weight sub-tiles of 256), waves 1 x 4.  Every wave owns
+// 128 rows x 128 columns either way.
+template <int WT, bool HALF>
 struct Cfg : TCfg<WT> {
   using T = TCfg<WT>;
-  static constexpr int A_STAGE_BYTES = BM * TBK * 2;
-  static constexpr int B_STAGE_BYTES = TBK * TBN * T::ESZ;
-  static constexpr int STAGE_BYTES = A_STAGE_BYTES + B_STAGE_BYTES;
+  static constexpr int TM = HALF ? 128 : 256;
+  static constexpr int NSUB = HALF ? 2 : 1;
+  static constexpr int A_STAGE_BYTES = TM * TBK * 2;
+  static constexpr int B_SUB_BYTES = TBK * TBN * T::ESZ;
   static constexpr int A_DPT = A_STAGE_BYTES / (256 * 16);  // direct loads per thread
-  static constexpr int B_DPT = B_STAGE_BYTES / (256 * 16);
+  static constexpr int B_SUB_DPT = B_SUB_BYTES / (256 * 16);
+  static constexpr int B_DPT = NSUB * B_SUB_DPT;
   static constexpr int DPT = A_DPT + B_DPT;
   static constexpr int NREAD = MI + 8 * T::RD_PER_FRAG;      // LDS reads per wave per step
-  static constexpr int LDS_BYTES = T::STAGES * STAGE_BYTES;
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert((T::STAGES - 2) * DPT < 64, "vmcnt field");
+};
+// one LDS ring serves both shapes: a stage holds the larger of the two
+template <int WT>
+struct Ring {
+  using F = Cfg<WT, false>;
+  using H = Cfg<WT, true>;
+  static constexpr int FB = F::A_STAGE_BYTES + F::NSUB * F::B_SUB_BYTES;
+  static constexpr int HB = H::A_STAGE_BYTES + H::NSUB * H::B_SUB_BYTES;
+  static constexpr int STAGE_BYTES = FB > HB ? FB : HB;
+  static constexpr int LDS_BYTES = TCfg<WT>::STAGES * STAGE_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
 constexpr int vmcnt_imm(int n) {
@@ -226,52 +244,35 @@ constexpr int slot_of(int i, int n, int span) { return (i * span) / n; }
 
 }  // namespace
 
-template <int EPI, int WT>
-__global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
-  using C = Cfg<WT>;
+// One tile: rows [p0, p0 + TM) of expert e's slots against weight sub-tiles
+// nt .. nt + NSUB - 1 (256 columns each), over the k-range of split ks (down
+// only: the fp32 sums of split ks go to its own output plane, which the
+// combine adds up; gate|up always has one split).  Called by all 256 threads after a
+// barrier that frees the LDS ring.  Thread 0 claims the workgroup's next tile
+// from *next as the tile starts and returns the counter's old value; other
+// threads return 0.
+template <int EPI, int WT, bool HALF>
+__device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint32_t lds_base,
+                                        int p0, int e, int nt, int ks, int* next) {
+  using C = Cfg<WT, HALF>;
   constexpr int S = C::STAGES;
   constexpr int ESZ = C::ESZ;
-  constexpr int CH = C::CHUNKS;    // 16-byte chunks per weight-tile row
+  constexpr int CH = C::CHUNKS;    // 16-byte chunks per weight sub-tile row
   constexpr int EPC = 16 / ESZ;    // weight elements per chunk
-  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int STB = Ring<WT>::STAGE_BYTES;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  // full: 2 x 2 waves; half: 1 x 4, waves 2j and 2j+1 on weight sub-tile j
+  const int wm = HALF ? 0 : wave >> 1;
+  const int wn = wave & 1;
+  const int sub = HALF ? wave >> 1 : 0;
+  const int ntw = nt + sub;        // the wave's 256-column tile
   const int lm = lane & 15, lg = lane >> 4;
-  const uint32_t lds_base = lds_off(lds);
-
-  // ---------------------------------------------------- tiles of this workgroup
-  // Persistent: one workgroup per compute unit loops over the tiles of the
-  // row blocks actually in use (their count is read from the device, so no
-  // workgroups are spent on the worst-case capacity's empty blocks).  Tiles
-  // are numbered with GROUP_M row blocks walked before the next weight tile.
-  // The dispatcher deals workgroups to the dies round-robin, each die with
-  // its own L2: every die takes an equal contiguous share of that numbering,
-  // so the workgroups a die runs at once share weight tiles and token blocks
-  // in its L2 instead of each die fetching every weight tile.
-  const int n_blocks = p.padded_rows != nullptr ? min(*p.padded_rows / BM, p.num_mblocks)
-                                                : p.num_mblocks;
-  const int n_work = n_blocks * p.n_tiles;
-  const int nwg = gridDim.x;
-  const int xcd = blockIdx.x % NXCD, li = blockIdx.x / NXCD;
-  const int q = nwg / NXCD, rem = nwg % NXCD;
-  const int on_die = q + (xcd < rem ? 1 : 0);
-  const int before = xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q;
-  const int w_begin = (int)((int64_t)n_work * before / nwg);
-  const int w_end = (int)((int64_t)n_work * (before + on_die) / nwg);
-  const int per_group = GROUP_M * p.n_tiles;
-  const int nk = p.K / TBK;
-  for (int id = w_begin + li; id < w_end; id += on_die) {
-  // the previous tile's LDS stages are free once every wave is done with them
-  __syncthreads();
-  const int grp = id / per_group;
-  const int first_mb = grp * GROUP_M;
-  const int gm = min(GROUP_M, n_blocks - first_mb);
-  const int local = id - grp * per_group;
-  const int mb = first_mb + local % gm;
-  const int nt = local / gm;
-  const int e = p.block_expert[mb];
-  const int p0 = mb * BM;
+  const int nk = p.kchunk / TBK;
+  const int64_t k0 = (int64_t)ks * p.kchunk;
+  // the workgroup's next tile, claimed now so the counter's latency hides
+  // behind this tile (before any accumulator is live)
+  const int claimed = tid == 0 ? atomicAdd(next, 1) : 0;
 
   // ---------------------------------------------------- direct-load sources
   // A slot s = (wave*A_DPT + i)*64 + lane -> tile row s/4, position s%4 =
@@ -284,15 +285,16 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
     int row = 0;  // padding rows read row 0; their results are never stored
     if (sid >= 0) row = (p.a_mode == A_GATHER) ? sid / p.topk : p0 + r;
     const int c = (lane & 3) ^ swz_a(r);
-    a_src[i] = reinterpret_cast<const char*>(p.a) + ((int64_t)row * p.a_ld + 8 * c) * 2;
+    a_src[i] = reinterpret_cast<const char*>(p.a) + ((int64_t)row * p.a_ld + k0 + 8 * c) * 2;
   }
-  // B slot s = (wave*B_DPT + i)*64 + lane -> k row s/CH, position s%CH; for
-  // gate|up the first half of a row's chunks are the h-tile's gate columns,
-  // the second half the matching up columns
-  const char* b_src[C::B_DPT];
+  // B slot of sub-tile 0: s = (wave*B_SUB_DPT + i)*64 + lane -> k row s/CH,
+  // position s%CH; for gate|up the first half of a row's chunks are the
+  // h-tile's gate columns, the second half the matching up columns.  Sub-tile
+  // j's slots read the same rows SUB_OFF * j bytes further on.
+  const char* b_src[C::B_SUB_DPT];
 #pragma unroll
-  for (int i = 0; i < C::B_DPT; ++i) {
-    const int r = (wave * C::B_DPT + i) * (64 / CH) + lane / CH;
+  for (int i = 0; i < C::B_SUB_DPT; ++i) {
+    const int r = (wave * C::B_SUB_DPT + i) * (64 / CH) + lane / CH;
     const int c = (lane % CH) ^ swz_b<WT>(r);
     int col;
     if constexpr (EPI == EPI_SILU_MUL)
@@ -300,19 +302,22 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
     else
       col = nt * TBN + EPC * c;
     b_src[i] = reinterpret_cast<const char*>(p.w) +
-               ((int64_t)e * p.w_estride + (int64_t)r * p.w_ld + col) * ESZ;
+               ((int64_t)e * p.w_estride + (k0 + r) * p.w_ld + col) * ESZ;
   }
+  constexpr int SUB_OFF = (EPI == EPI_SILU_MUL ? 128 : TBN) * ESZ;
   const int64_t b_kstep = (int64_t)TBK * p.w_ld * ESZ;  // bytes per k-step of B
 
   // the d-th direct load (of DPT) of k-step kt into stage st
   auto dma = [&](auto d_c, int st, int kt) __attribute__((always_inline)) {
     constexpr int d = decltype(d_c)::value;
-    char* sa = lds + st * C::STAGE_BYTES;
+    char* sa = lds + st * STB;
     if constexpr (d < C::A_DPT) {
       dma16(a_src[d] + (int64_t)kt * (TBK * 2), sa + (wave * C::A_DPT + d) * 1024);
     } else {
       constexpr int i = d - C::A_DPT;
-      dma16(b_src[i] + kt * b_kstep, sa + C::A_STAGE_BYTES + (wave * C::B_DPT + i) * 1024);
+      constexpr int j = i / C::B_SUB_DPT, ii = i % C::B_SUB_DPT;
+      dma16(b_src[ii] + kt * b_kstep + j * SUB_OFF,
+            sa + C::A_STAGE_BYTES + j * C::B_SUB_BYTES + (wave * C::B_SUB_DPT + ii) * 1024);
     }
   };
   auto dma_all = [&](int st, int kt) __attribute__((always_inline)) {
@@ -320,16 +325,17 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
   };
 
   // ---------------------------------------------------- fragment addresses
-  // A fragment mi: row R = wm*BM/2 + mi*16 + lane%16, chunk lane/16.
+  // A fragment mi: row R = wm*128 + mi*16 + lane%16, chunk lane/16.
   // R%16 = lane%16, so the swizzle is the lane's own and the address is a
   // per-lane base plus the immediate mi*1024.
-  const uint32_t a_base = (uint32_t)(((wm * (BM / 2) + lm) * 4 + (lg ^ swz_a(lm))) * 16);
+  const uint32_t a_base = (uint32_t)(((wm * 128 + lm) * 4 + (lg ^ swz_a(lm))) * 16);
   // B fragment ni covers chunk c0(ni) (fp8: 16 columns) or chunks c0(ni),
-  // c0(ni)+1 (bf16) of the wave's columns.
+  // c0(ni)+1 (bf16) of the wave's columns in its sub-tile.
   //   bf16, half h: k row 8*lg + lm/4 + 4h, chunk c0 + (lm%4)/2, 8-byte half
   //   lm&1; swz of that row depends only on lm/4 and lg&1 (the lane's own),
   //   h is the immediate 4 rows.
   //   fp8: k row 8*lg + lm/2, chunk c0, 8-byte half lm&1.
+  const uint32_t b_region = (uint32_t)(C::A_STAGE_BYTES + sub * C::B_SUB_BYTES);
   uint32_t b_base[8];
 #pragma unroll
   for (int ni = 0; ni < 8; ++ni) {
@@ -340,8 +346,7 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
       else
         c0 = wn * 8 + ni;
       const int row = 8 * lg + (lm >> 1);
-      b_base[ni] = (uint32_t)((row * CH + (c0 ^ swz_b<WT>(row))) * 16 + (lm & 1) * 8) +
-                   C::A_STAGE_BYTES;
+      b_base[ni] = (uint32_t)((row * CH + (c0 ^ swz_b<WT>(row))) * 16 + (lm & 1) * 8) + b_region;
     } else {
       int c0;
       if constexpr (EPI == EPI_SILU_MUL)
@@ -351,7 +356,7 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
       const int row = 8 * lg + (lm >> 2);
       const int xb = swz_b<WT>(row);
       b_base[ni] = (uint32_t)((row * CH + ((c0 ^ xb) + ((lm & 3) >> 1))) * 16 + (lm & 1) * 8) +
-                   C::A_STAGE_BYTES;
+                   b_region;
     }
   }
 
@@ -430,11 +435,11 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * C::DPT));
     __builtin_amdgcn_s_barrier();
     const int refill_kt = kt + S < nk ? kt + S : kt;
-    step(first_c, cur, wcur, nxt, lds_base + ((kt + 1) % S) * C::STAGE_BYTES, kt % S, refill_kt);
+    step(first_c, cur, wcur, nxt, lds_base + ((kt + 1) % S) * STB, kt % S, refill_kt);
     wait_frags(nxt);
     if constexpr (WT == W_FP8) widen_fp8(nxt.b, *reinterpret_cast<u32x4(*)[8]>(wnxt));
   };
-  // nk is even (K is a multiple of 64): step 0, pairs (1, 2) ... (nk-3, nk-2),
+  // nk is even (a split is a multiple of 64 deep): step 0, pairs (1, 2) ... (nk-3, nk-2),
   // then step nk-1
   one(std::true_type{}, f0, w0, f1, w1, 0);
   for (int kt = 1; kt + 1 < nk; kt += 2) {
@@ -453,28 +458,29 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
   // ---------------------------------------------------- epilogue
   // acc[mi][ni]: lane (n = lane%16, g = lane/16) holds rows 4g + r of the 16x16
   // block (mi, ni).  Lane columns: gate|up ni < 4: gate column
-  // nt*128 + wn*64 + 16ni + lm, ni >= 4 the matching up column; down:
-  // nt*256 + wn*128 + 16ni + lm.
+  // ntw*128 + wn*64 + 16ni + lm, ni >= 4 the matching up column; down:
+  // ntw*256 + wn*128 + 16ni + lm.
   float sc[8];  // fp8: per-column scales of the lane's 8 columns
   if constexpr (WT == W_FP8) {
     const float* sb = p.scale + (int64_t)e * p.scale_estride;
 #pragma unroll
     for (int ni = 0; ni < 8; ++ni) {
       if constexpr (EPI == EPI_SILU_MUL)
-        sc[ni] = sb[(ni < 4 ? 0 : p.up_off) + nt * 128 + wn * 64 + 16 * (ni & 3) + lm];
+        sc[ni] = sb[(ni < 4 ? 0 : p.up_off) + ntw * 128 + wn * 64 + 16 * (ni & 3) + lm];
       else
-        sc[ni] = sb[nt * TBN + wn * 128 + 16 * ni + lm];
+        sc[ni] = sb[ntw * TBN + wn * 128 + 16 * ni + lm];
     }
   }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int lrow = wm * (BM / 2) + mi * 16 + 4 * lg + r;
+      const int lrow = wm * 128 + mi * 16 + 4 * lg + r;
       if (p.sorted_ids[p0 + lrow] < 0) continue;
       const int64_t prow = p0 + lrow;
       if constexpr (EPI == EPI_SILU_MUL) {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + prow * p.out_ld + nt * 128 + wn * 64 + lm;
+        uint16_t* dst =
+            reinterpret_cast<uint16_t*>(p.out) + prow * p.out_ld + ntw * 128 + wn * 64 + lm;
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
           float g = acc[mi][ni][r], u = acc[mi][ni + 4][r];
@@ -485,7 +491,8 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
           dst[ni * 16] = (uint16_t)f32_to_bf16_bits(silu(g) * u);
         }
       } else {
-        float* dst = reinterpret_cast<float*>(p.out) + prow * p.out_ld + nt * TBN + wn * 128 + lm;
+        float* dst = reinterpret_cast<float*>(p.out) + ks * p.out_split_stride + prow * p.out_ld +
+                     ntw * TBN + wn * 128 + lm;
 #pragma unroll
         for (int ni = 0; ni < 8; ++ni) {
           float v = acc[mi][ni][r];
@@ -494,17 +501,97 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
         }
       }
     }
+  return claimed;
+}
+
+template <int EPI, int WT>
+__global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const uint32_t lds_base = lds_off(lds);
+
+  // ---------------------------------------------------- tiles of this workgroup
+  // Persistent: one workgroup per compute unit takes tiles of the rows the
+  // alignment listed (their counts are read from the device, so no
+  // workgroups are spent on the worst-case capacity).  Full rows come first,
+  // n_tiles tiles each, then half rows, n_tiles/2 tiles each; within each
+  // kind, GROUP_M rows are walked before the next weight tile.  The
+  // dispatcher deals workgroups to the dies round-robin, each die with its
+  // own L2: every die takes a contiguous share of that numbering, so the
+  // workgroups a die runs at once share weight tiles and token blocks in its
+  // L2 instead of each die fetching every weight tile.  The shares are equal
+  // in cost, a half tile counting 5/4 of a full one (its 128 x 512 tile
+  // issues more loads per MFMA; measured 1.1-1.3x a full tile's time), and
+  // within a die the workgroups claim the share's tiles in order from the
+  // die's counter, so unequal tiles still end together.
+  // With k-splits (down only) the numbering repeats once per split.
+  const int n_full = min(p.tile_counts[0], p.num_mblocks);
+  const int n_half = min(p.tile_counts[1], p.num_mblocks - n_full);
+  const int nt_half = p.n_tiles / 2;
+  const int work_full = n_full * p.n_tiles;
+  const int work1 = work_full + n_half * nt_half;  // tiles of one split
+  const int64_t cost_full = 4 * (int64_t)work_full;
+  const int64_t cost1 = cost_full + 5 * (int64_t)n_half * nt_half;
+  const int64_t cost = cost1 * p.ksplit;
+  // first tile whose cost range starts at or after c
+  auto tile_at = [&](int64_t c) -> int {
+    if (cost1 == 0) return 0;
+    const int ks = (int)(c / cost1);
+    const int64_t r = c - ks * cost1;
+    return ks * work1 +
+           (r <= cost_full ? (int)((r + 3) / 4) : work_full + (int)((r - cost_full + 4) / 5));
+  };
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x % NXCD;
+  const int q = nwg / NXCD, rem = nwg % NXCD;
+  const int on_die = q + (xcd < rem ? 1 : 0);
+  const int before = xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q;
+  const int w_begin = tile_at(cost * before / nwg);
+  const int w_end = tile_at(cost * (before + on_die) / nwg);
+  int* next = p.die_next + xcd;
+  // thread 0's claim goes to every thread through a word of the (then idle)
+  // LDS ring; the second barrier keeps the next tile's loads from
+  // overwriting it before every wave has read it
+  int* s_claim = reinterpret_cast<int*>(lds);
+  auto publish = [&](int v) __attribute__((always_inline)) {
+    if (threadIdx.x == 0) s_claim[0] = v;
+    __syncthreads();
+    const int r = s_claim[0];
+    __syncthreads();
+    return r;
+  };
+  int id = w_begin + publish(threadIdx.x == 0 ? atomicAdd(next, 1) : 0);
+  while (id < w_end) {
+    const int ks = id / work1;
+    const int t = id - ks * work1;
+    const bool full = t < work_full;
+    const int rows = full ? n_full : n_half;
+    const int nts = full ? p.n_tiles : nt_half;
+    const int lid = full ? t : t - work_full;
+    const int per_group = GROUP_M * nts;
+    const int grp = lid / per_group;
+    const int first = grp * GROUP_M;
+    const int gm = min(GROUP_M, rows - first);
+    const int local = lid - grp * per_group;
+    const int row = (full ? 0 : n_full) + first + local % gm;
+    const int nt = local / gm;
+    const int p0 = p.tile_rows[2 * row];
+    const int e = p.tile_rows[2 * row + 1];
+    const int claimed = full ? run_tile<EPI, WT, false>(p, lds, lds_base, p0, e, nt, ks, next)
+                             : run_tile<EPI, WT, true>(p, lds, lds_base, p0, e, 2 * nt, ks, next);
+    // every wave is done with the tile's LDS stages
+    __syncthreads();
+    id = w_begin + publish(claimed);
   }
 }
 
 template <int EPI, int WT>
 static hipError_t launch_tiled(const StreamGemmArgs& a, hipStream_t st) {
-  const int64_t work = (int64_t)a.num_mblocks * a.n_tiles;
+  const int64_t work = (int64_t)a.num_mblocks * a.n_tiles * a.ksplit;
   if (work <= 0) return hipSuccess;
   if (work > 0x7FFFFFFF) return hipErrorInvalidValue;
   // one resident workgroup per compute unit
   const int64_t grid = std::min<int64_t>(work, device_cus());
-  constexpr int lds = Cfg<WT>::LDS_BYTES;
+  constexpr int lds = Ring<WT>::LDS_BYTES;
   hipError_t e = hipFuncSetAttribute((const void*)k_expert_tiled<EPI, WT>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
@@ -514,7 +601,15 @@ static hipError_t launch_tiled(const StreamGemmArgs& a, hipStream_t st) {
 
 hipError_t launch_tiled_gemm(int epi, int w_dtype, int bm, const StreamGemmArgs& a,
                              hipStream_t st) {
-  if (bm != BM || a.K % 64 != 0) return hipErrorInvalidValue;
+  // half rows (bm = 128) pair two 256-column tiles: n_tiles must be even
+  if ((bm != 256 && bm != 128) || a.K % 64 != 0) return hipErrorInvalidValue;
+  // k-splits: down only, each a multiple of 64 deep
+  if (a.ksplit < 1 || a.kchunk % 64 != 0 || (int64_t)a.ksplit * a.kchunk != a.K ||
+      (epi == EPI_SILU_MUL && a.ksplit != 1))
+    return hipErrorInvalidValue;
+  if (bm == 128 && a.n_tiles % 2 != 0) return hipErrorInvalidValue;
+  if (a.tile_rows == nullptr || a.tile_counts == nullptr || a.die_next == nullptr)
+    return hipErrorInvalidValue;
   if (w_dtype == W_FP8) {
     if (a.scale == nullptr) return hipErrorInvalidValue;
     return epi == EPI_SILU_MUL ? launch_tiled<EPI_SILU_MUL, W_FP8>(a, st)

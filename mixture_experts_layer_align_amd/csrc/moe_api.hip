@@ -85,11 +85,6 @@ int choose_kchunk(int64_t items, int K, int kstep, int* nsplit, int below, int t
   return chunk_steps * kstep;
 }
 
-// Number of k-splits for a weight-streaming GEMM of `items` workgroups when
-// fewer than `below` would run: every split adds a workgroup per item, and
-// the layer takes as long as its busiest compute unit, whose share of the
-// work is ceil(items*s / cus) / s (workgroups of equal size, spread evenly).
-// The smallest s with the least share wins; at least min_steps k-steps each.
 // Workgroups of a persistent stream GEMM launch over `items` expected items:
 // as many as leave every workgroup the same whole number of items, at most
 // one per compute unit; 0 (one workgroup per item) when there are fewer items
@@ -100,6 +95,11 @@ int persistent_wgs(int64_t items, int cus) {
   return (int)((items + per - 1) / per);
 }
 
+// Number of k-splits for a weight-streaming GEMM of `items` workgroups when
+// fewer than `below` would run: every split adds a workgroup per item, and
+// the layer takes as long as its busiest compute unit, whose share of the
+// work is ceil(items*s / cus) / s (workgroups of equal size, spread evenly).
+// The smallest s with the least share wins; at least min_steps k-steps each.
 int choose_kchunk_balanced(int64_t items, int K, int kstep, int* nsplit, int below, int min_steps,
                            int max_split, int cus) {
   const int steps = K / kstep;
@@ -119,6 +119,28 @@ int choose_kchunk_balanced(int64_t items, int K, int kstep, int* nsplit, int bel
   const int chunk_steps = (steps + best - 1) / best;
   *nsplit = (steps + chunk_steps - 1) / chunk_steps;
   return chunk_steps * kstep;
+}
+
+// k-splits of the tiled down GEMM over `tiles` expected tiles: the busiest
+// compute unit's share, ceil(tiles*s / cus) / s full-depth tiles, against the
+// cost of each further fp32 output plane (written here and read again by the
+// combine, 8 bytes per routed row and output column at ~5.5 TB/s, against
+// 2*K flops per row and column at ~1.3 PFLOP/s: 945/K of the GEMM's ideal
+// time per plane).  Each split is a multiple of 64 deep; at most 4.
+int choose_tiled_split(int64_t tiles, int K, int cus) {
+  tiles = std::max<int64_t>(tiles, 1);
+  const double ideal = (double)tiles / cus;
+  int best = 1;
+  double best_t = 1e30;
+  for (int s = 1; s <= 4; ++s) {
+    if (K % (64 * s) != 0) continue;
+    const double t = (double)((tiles * s + cus - 1) / cus) / s + (s - 1) * ideal * 945.0 / K;
+    if (t < best_t * (1.0 - 1e-9)) {
+      best_t = t;
+      best = s;
+    }
+  }
+  return best;
 }
 
 // ------------------------------------------------------------ router plan
@@ -329,7 +351,10 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   const bool tiled = act == ACT_BF16 && (wdt == W_BF16 || wdt == W_FP8) &&
                      n >= (int64_t)TILED_MIN_ROWS * E &&
                      d % TILED_BN == 0 && dff % (TILED_BN / 2) == 0;
-  const int bm = tiled ? TILED_BM : STREAM_BM;
+  // the tiled GEMM's half tiles pair two 256-column tiles, so experts are
+  // padded to 128 rows when both GEMMs have an even number of column tiles
+  const bool half_rows = tiled && (dff / (TILED_BN / 2)) % 2 == 0 && (d / TILED_BN) % 2 == 0;
+  const int bm = tiled ? (half_rows ? TILED_BM / 2 : TILED_BM) : STREAM_BM;
   const int64_t cap = moe_align_capacity(T, E, k, bm);
   const int64_t nblocks = cap / bm;
 
@@ -360,6 +385,13 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
       gu_wgs = persistent_wgs(gu_items * gu_split, cus);
       dn_wgs = persistent_wgs(dn_items * dn_split, cus);
     }
+  } else {
+    // tile rows: one per 256 routed rows plus about half a row of padding per
+    // active expert
+    const int64_t rows_est =
+        std::min<int64_t>(nblocks, (n + 255) / 256 + std::min<int64_t>(E, n) / 2);
+    dn_split = choose_tiled_split(rows_est * dn_tiles, dff, device_cus());
+    dn_chunk = dff / dn_split;
   }
   Carve c(workspace);
   float* r_partial = c.take<float>(std::max<int64_t>(r.partial_floats, 1));
@@ -371,6 +403,9 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   int32_t* inv = c.take<int32_t>(std::max<int64_t>(n, 1));
   int32_t* bexp = c.take<int32_t>(std::max<int64_t>(nblocks, 1));
   char* al_ws = c.take<char>(std::max<int64_t>(align_workspace_bytes((int)n, E), 1));
+  // tiled GEMM row list: at most one row per bm-block
+  int32_t* trows = tiled ? c.take<int32_t>(2 * std::max<int64_t>(nblocks, 1)) : nullptr;
+  int32_t* tcounts = tiled ? c.take<int32_t>(2 + TILE_COUNTERS) : nullptr;
   char* h = c.take<char>(std::max<int64_t>(cap * dff * ab, 1));
   // per-slot expert outputs (fp32), or their k-split partial sums
   float* y = c.take<float>(std::max<int64_t>(dn_split * cap * d, 1));
@@ -411,6 +446,8 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   a.sorted_ids = sorted;
   a.inv_pos = inv;
   a.block_expert = bexp;
+  a.tile_rows = trows;
+  a.tile_counts = tcounts;
   hipError_t e;
   if (route_align_small_ok(T, E, k, r.nsplit)) {
     // a few tokens: top-k and alignment in one launch
@@ -439,6 +476,9 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g.block_expert = bexp;
   g.num_mblocks = (int)nblocks;
   g.padded_rows = offs + E;
+  g.tile_rows = trows;
+  g.tile_counts = tcounts;
+  g.die_next = tiled ? tcounts + 2 : nullptr;
   g.w = L->w_gate_up;
   g.w_ld = 2 * (int64_t)dff;
   g.w_estride = (int64_t)d * 2 * dff;
@@ -477,6 +517,9 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g2.block_expert = bexp;
   g2.num_mblocks = (int)nblocks;
   g2.padded_rows = offs + E;
+  g2.tile_rows = trows;
+  g2.tile_counts = tcounts;
+  g2.die_next = tiled ? tcounts + 2 + TILE_COUNTERS / 2 : nullptr;
   g2.w = L->w_down;
   g2.w_ld = d;
   g2.w_estride = (int64_t)dff * d;
@@ -491,6 +534,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g2.partial = y;
   g2.partial_ld = d;
   g2.partial_split_stride = cap * d;
+  g2.out_split_stride = cap * d;
   g2.out = y;
   g2.out_ld = d;
   trace_mark(tr, &kidx, "down", st);

@@ -58,6 +58,10 @@ struct StreamGemmArgs {
   int64_t out_split_stride;  // router: elements between split planes
   int wgs;                // stream GEMM: workgroups, each looping over items
                           //   g, g + wgs, ...; 0 = one workgroup per item
+  const int32_t* tile_rows;    // tiled GEMM: [rows][2] = {first slot, expert}, full rows
+                               //   (256 slots) first, then half rows (128 slots)
+  const int32_t* tile_counts;  // tiled GEMM: {full rows, half rows} (device)
+  int32_t* die_next;           // tiled GEMM: 8 per-die tile counters, zero at launch
 };
 
 // Compute units of the current device (cached per device; 256 if the query
@@ -113,11 +117,20 @@ struct AlignArgs {
   int32_t* sorted_ids;
   int32_t* inv_pos;
   int32_t* block_expert;
+  // optional (NULL: not written): the row list of the tiled expert GEMM.  An
+  // expert's padded slots are cut into 256-slot rows, the last one 128 slots
+  // when 128 remain (bm = 128); full rows are listed first, then half rows,
+  // each as {first slot, expert}; tile_counts = {full rows, half rows, then
+  // TILE_COUNTERS zeros: the two tiled GEMMs' per-die tile counters}
+  int32_t* tile_rows;
+  int32_t* tile_counts;
   // multi-tile scratch
   int32_t* tile_hist;   // [ntiles][E]
   int32_t* rank;        // [n]
   int ntiles;
 };
+
+constexpr int TILE_COUNTERS = 16;
 
 constexpr int ALIGN_SINGLE_MAX = 4096;   // entries one workgroup aligns alone
 constexpr int ALIGN_TILE = 4096;         // entries per tile of the multi-pass path

@@ -289,9 +289,10 @@ __device__ int hist_wave_prefix(int* hist, int E) {
   return run;
 }
 
-// counts/offsets known (in LDS): write counts, offsets, padding -1 slots and
-// block_expert.  Called by one workgroup.
-__device__ void write_layout(const AlignArgs& a, const int* s_counts, const int* s_off) {
+// counts/offsets known (in LDS): write counts, offsets, padding -1 slots,
+// block_expert and, if asked for, the tiled GEMM's row list.  Called by every
+// thread of one workgroup (E <= AL_THREADS); sh is scan scratch.
+__device__ void write_layout(const AlignArgs& a, const int* s_counts, const int* s_off, int* sh) {
   const int E = a.E, bm = a.bm;
   for (int e = threadIdx.x; e < E; e += AL_THREADS) {
     a.counts[e] = s_counts[e];
@@ -303,6 +304,33 @@ __device__ void write_layout(const AlignArgs& a, const int* s_counts, const int*
   for (int64_t s = s_off[E] + threadIdx.x; s < a.cap; s += AL_THREADS) a.sorted_ids[s] = -1;
   for (int64_t b = s_off[E] / bm + threadIdx.x; b < a.cap / bm; b += AL_THREADS)
     a.block_expert[b] = -1;
+  if (a.tile_rows == nullptr) return;
+  // rows of 256 slots; a remainder (128 slots when bm = 128) is a half row
+  const int e = threadIdx.x;
+  int nf = 0, nh = 0;
+  if (e < E) {
+    const int pad = s_off[e + 1] - s_off[e];
+    nf = pad / 256;
+    nh = pad % 256 != 0 ? 1 : 0;
+  }
+  int tot_f, tot_h;
+  const int bf = block_exscan(nf, sh, &tot_f);
+  const int bh = block_exscan(nh, sh, &tot_h);
+  if (e < E) {
+    for (int r = 0; r < nf; ++r) {
+      a.tile_rows[2 * (bf + r)] = s_off[e] + 256 * r;
+      a.tile_rows[2 * (bf + r) + 1] = e;
+    }
+    if (nh != 0) {
+      a.tile_rows[2 * (tot_f + bh)] = s_off[e] + 256 * nf;
+      a.tile_rows[2 * (tot_f + bh) + 1] = e;
+    }
+  }
+  if (threadIdx.x == 0) {
+    a.tile_counts[0] = tot_f;
+    a.tile_counts[1] = tot_h;
+  }
+  if (threadIdx.x < TILE_COUNTERS) a.tile_counts[2 + threadIdx.x] = 0;
 }
 
 __device__ __forceinline__ int ilog2_ceil(int E) {
@@ -341,7 +369,7 @@ __device__ void align_one_tile(const AlignArgs& a, const int32_t* ids, int* lds)
     a.sorted_ids[pos] = i;
     a.inv_pos[i] = pos;
   }
-  write_layout(a, s_counts, s_off);
+  write_layout(a, s_counts, s_off, sh);
 }
 
 __global__ __launch_bounds__(AL_THREADS) void k_align_single(const AlignArgs a) {
@@ -546,7 +574,7 @@ __global__ __launch_bounds__(AL_THREADS) void k_align_scatter(const AlignArgs a)
     a.sorted_ids[pos] = (int)i;
     a.inv_pos[i] = pos;
   }
-  if (blockIdx.x == 0) write_layout(a, s_counts, s_off);
+  if (blockIdx.x == 0) write_layout(a, s_counts, s_off, sh);
 }
 
 int64_t align_workspace_bytes(int n, int E) {

@@ -116,6 +116,31 @@ def test_forward_all_tokens_on_one_expert_in_full_blocks(T):
     assert bm == (256 if T == 1024 else 32)
 
 
+HALF_ROWS = [
+    # E, k, d, d_ff, wdt, T, zipf: both GEMMs have an even number of 256-column
+    # tiles, so experts are padded to 128 rows and an expert's last 128 rows
+    # run as a half tile (128 rows x 512 columns)
+    (8, 2, 512, 256, "bf16", 700, 1.2),
+    (16, 4, 1024, 512, "bf16", 1500, 1.0),
+    (8, 2, 512, 512, "fp8", 900, 1.2),
+    (32, 4, 512, 256, "fp8", 1600, 0.6),
+]
+
+
+@pytest.mark.parametrize("E,k,d,d_ff,wdt,T,zipf", HALF_ROWS)
+def test_forward_tiled_half_rows(E, k, d, d_ff, wdt, T, zipf):
+    sh = LayerShape(260 + E, "half-rows", E=E, k=k, d=d, d_ff=d_ff, act="bf16", wdt=wdt,
+                    seed=40 + E + T)
+    print(f"forward half rows E={E} k={k} d={d} d_ff={d_ff} {wdt} T={T}", flush=True)
+    layer = make_layer(sh, T, "cuda", zipf=zipf)
+    x = make_tokens(sh, T, "cuda")
+    _, rb, bm = run_and_check(layer, x, what="half rows")
+    assert bm == 128
+    rem = rb["counts"].cpu().numpy() % 256
+    assert ((rem > 0) & (rem <= 128)).any(), "no expert ends in a half row"
+    assert (rem > 128).any(), "no expert ends in a partly filled full row"
+
+
 def test_forward_is_deterministic():
     sh = CONFIGS[3]
     layer = make_layer(sh, 256, "cuda")
