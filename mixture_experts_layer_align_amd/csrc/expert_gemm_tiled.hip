@@ -253,7 +253,8 @@ constexpr int slot_of(int i, int n, int span) { return (i * span) / n; }
 // threads return 0.
 template <int EPI, int WT, bool HALF>
 __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint32_t lds_base,
-                                        int p0, int e, int nt, int ks, int* next) {
+                                        int p0, int e, int n_valid, int nt, int ks,
+                                        int* next) {
   using C = Cfg<WT, HALF>;
   constexpr int S = C::STAGES;
   constexpr int ESZ = C::ESZ;
@@ -471,12 +472,15 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
         sc[ni] = sb[ntw * TBN + wn * 128 + 16 * ni + lm];
     }
   }
+  // the lane's row wm*128 + 4*lg + (mi*16 + r) holds a routed slot iff
+  // mi*16 + r < vrows (a compile-time offset against one register)
+  const int vrows = n_valid - (wm * 128 + 4 * lg);
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+      if (mi * 16 + r >= vrows) continue;  // padding slot
       const int lrow = wm * 128 + mi * 16 + 4 * lg + r;
-      if (p.sorted_ids[p0 + lrow] < 0) continue;
       const int64_t prow = p0 + lrow;
       if constexpr (EPI == EPI_SILU_MUL) {
         uint16_t* dst =
@@ -555,7 +559,8 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
   auto publish = [&](int v) __attribute__((always_inline)) {
     if (threadIdx.x == 0) s_claim[0] = v;
     __syncthreads();
-    const int r = s_claim[0];
+    // uniform across the workgroup: keep it (and the tile's indices) scalar
+    const int r = __builtin_amdgcn_readfirstlane(s_claim[0]);
     __syncthreads();
     return r;
   };
@@ -575,9 +580,11 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
     const int row = (full ? 0 : n_full) + first + local % gm;
     const int nt = local / gm;
     const int p0 = p.tile_rows[2 * row];
-    const int e = p.tile_rows[2 * row + 1];
-    const int claimed = full ? run_tile<EPI, WT, false>(p, lds, lds_base, p0, e, nt, ks, next)
-                             : run_tile<EPI, WT, true>(p, lds, lds_base, p0, e, 2 * nt, ks, next);
+    const int ev = p.tile_rows[2 * row + 1];
+    const int e = ev & 0xFFFF, n_valid = ev >> 16;
+    const int claimed =
+        full ? run_tile<EPI, WT, false>(p, lds, lds_base, p0, e, n_valid, nt, ks, next)
+             : run_tile<EPI, WT, true>(p, lds, lds_base, p0, e, n_valid, 2 * nt, ks, next);
     // every wave is done with the tile's LDS stages
     __syncthreads();
     id = w_begin + publish(claimed);

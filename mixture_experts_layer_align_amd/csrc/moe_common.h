@@ -129,7 +129,14 @@ __device__ __forceinline__ void store_act(char* dst, const float* v, int nv) {
 
 // ------------------------------------------------------------ activation
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// SiLU(z) = z * sigmoid(z), from the hardware base-2 exponential and
+// reciprocal (a few fp32 ulps; h is rounded to bf16 or kept in fp32 against a
+// 1e-4 relative tolerance).  Large |z| reach the limits: exp2 overflows to
+// inf and the reciprocal to 0 for z << 0, and the sigmoid is 1 for z >> 0.
+__device__ __forceinline__ float silu(float z) {
+  constexpr float LOG2E = 1.4426950408889634f;
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * LOG2E));
+}
 
 // ------------------------------------------------------------ wave helpers
 

@@ -58,8 +58,9 @@ struct StreamGemmArgs {
   int64_t out_split_stride;  // router: elements between split planes
   int wgs;                // stream GEMM: workgroups, each looping over items
                           //   g, g + wgs, ...; 0 = one workgroup per item
-  const int32_t* tile_rows;    // tiled GEMM: [rows][2] = {first slot, expert}, full rows
-                               //   (256 slots) first, then half rows (128 slots)
+  const int32_t* tile_rows;    // tiled GEMM: [rows][2] = {first slot, expert | routed
+                               //   slots << 16}, full rows (256 slots) first, then half
+                               //   rows (128 slots); routed slots are the row's first ones
   const int32_t* tile_counts;  // tiled GEMM: {full rows, half rows} (device)
   int32_t* die_next;           // tiled GEMM: 8 per-die tile counters, zero at launch
 };
@@ -120,7 +121,7 @@ struct AlignArgs {
   // optional (NULL: not written): the row list of the tiled expert GEMM.  An
   // expert's padded slots are cut into 256-slot rows, the last one 128 slots
   // when 128 remain (bm = 128); full rows are listed first, then half rows,
-  // each as {first slot, expert}; tile_counts = {full rows, half rows, then
+  // each as {first slot, expert | routed slots of the row << 16}; tile_counts = {full rows, half rows, then
   // TILE_COUNTERS zeros: the two tiled GEMMs' per-die tile counters}
   int32_t* tile_rows;
   int32_t* tile_counts;

@@ -316,14 +316,17 @@ __device__ void write_layout(const AlignArgs& a, const int* s_counts, const int*
   int tot_f, tot_h;
   const int bf = block_exscan(nf, sh, &tot_f);
   const int bh = block_exscan(nh, sh, &tot_h);
+  // {first slot, expert | routed rows of the row << 16}: the routed slots of
+  // an expert come first in its range, so a row's routed slots are a prefix
   if (e < E) {
+    const int cnt = s_counts[e];
     for (int r = 0; r < nf; ++r) {
       a.tile_rows[2 * (bf + r)] = s_off[e] + 256 * r;
-      a.tile_rows[2 * (bf + r) + 1] = e;
+      a.tile_rows[2 * (bf + r) + 1] = e | (min(max(cnt - 256 * r, 0), 256) << 16);
     }
     if (nh != 0) {
       a.tile_rows[2 * (tot_f + bh)] = s_off[e] + 256 * nf;
-      a.tile_rows[2 * (tot_f + bh) + 1] = e;
+      a.tile_rows[2 * (tot_f + bh) + 1] = e | (min(max(cnt - 256 * nf, 0), 128) << 16);
     }
   }
   if (threadIdx.x == 0) {
