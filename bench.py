@@ -255,8 +255,8 @@ def qk_norm_bench(B, roof, dev, steps):
 def measured_traffic(kernel, sh, T):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     record for this workload (FETCH_SIZE and WRITE_SIZE scaled by a plain copy
-    of known size), or None when there is none or the kernel's source changed
-    since the counters were taken."""
+    of known size), or None when there is none or any source the kernel is
+    compiled from changed since the counters were taken."""
     import glob
     import hashlib
     want = f"E={sh.E} top-{sh.k} d={sh.d} d_ff={sh.d_ff} {sh.wdt} T={T}"
@@ -265,9 +265,14 @@ def measured_traffic(kernel, sh, T):
             rec = json.load(f)
         if rec.get("kernel") != kernel or rec.get("workload") != want:
             continue
-        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
-                return None
+        # every source the kernel is compiled from, as at measurement (a
+        # record without them cannot be matched to the code: stale)
+        if not rec.get("sources"):
+            return None
+        for src, sha in rec["sources"].items():
+            with open(os.path.join(ROOT, src), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != sha:
+                    return None
         return rec["traffic_bytes_per_launch"]
     return None
 

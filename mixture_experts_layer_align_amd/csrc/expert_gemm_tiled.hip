@@ -277,14 +277,18 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
 
   // ---------------------------------------------------- direct-load sources
   // A slot s = (wave*A_DPT + i)*64 + lane -> tile row s/4, position s%4 =
-  // lane%4 (64-slot blocks start at multiples of 4 rows)
+  // lane%4 (64-slot blocks start at multiples of 4 rows).  gate|up gathers
+  // token rows of x by slot; down reads h by slot directly (padding slots
+  // read their own rows of h, in bounds, and their results are never stored)
   const char* a_src[C::A_DPT];
 #pragma unroll
   for (int i = 0; i < C::A_DPT; ++i) {
     const int r = ((wave * C::A_DPT + i) * 64 + lane) >> 2;
-    const int sid = p.sorted_ids[p0 + r];
-    int row = 0;  // padding rows read row 0; their results are never stored
-    if (sid >= 0) row = (p.a_mode == A_GATHER) ? sid / p.topk : p0 + r;
+    int row = p0 + r;
+    if constexpr (EPI == EPI_SILU_MUL) {
+      const int sid = p.sorted_ids[p0 + r];
+      row = sid >= 0 ? sid / p.topk : 0;  // padding slots read token 0
+    }
     const int c = (lane & 3) ^ swz_a(r);
     a_src[i] = reinterpret_cast<const char*>(p.a) + ((int64_t)row * p.a_ld + k0 + 8 * c) * 2;
   }
@@ -617,6 +621,8 @@ hipError_t launch_tiled_gemm(int epi, int w_dtype, int bm, const StreamGemmArgs&
   if (bm == 128 && a.n_tiles % 2 != 0) return hipErrorInvalidValue;
   if (a.tile_rows == nullptr || a.tile_counts == nullptr || a.die_next == nullptr)
     return hipErrorInvalidValue;
+  // gate|up gathers tokens by slot, down reads its rows by slot
+  if (a.a_mode != (epi == EPI_SILU_MUL ? A_GATHER : A_PADDED)) return hipErrorInvalidValue;
   if (w_dtype == W_FP8) {
     if (a.scale == nullptr) return hipErrorInvalidValue;
     return epi == EPI_SILU_MUL ? launch_tiled<EPI_SILU_MUL, W_FP8>(a, st)
