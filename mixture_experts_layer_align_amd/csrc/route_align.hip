@@ -82,14 +82,18 @@ __device__ __forceinline__ void plane_sum_q(const float* __restrict__ pp, int ns
 
 // Top-k of one token per wave (tokens = 4 per workgroup) or, with WIDE, of
 // one token per workgroup whose 4 waves each own one of the 4 plane sums.
-template <int V, bool WIDE>
+// Selection r is kept by lane r (k <= 64), or in LDS with BIGK (k > 64);
+// either way the weights are computed from the same values in the same
+// order, so the bits do not depend on k's path.
+template <int V, bool WIDE, bool BIGK>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial, int nsplit,
                                               int64_t split_stride, const float* __restrict__ bias,
                                               int T, int E, int k, float* __restrict__ logits,
                                               int32_t* __restrict__ ids, float* __restrict__ wout) {
   __shared__ float part[WIDE ? 4 : 1][WIDE ? MAX_EXPERTS : 1];
-  __shared__ float sel_v[WIDE ? 1 : 4][MAX_EXPERTS];
-  __shared__ int sel_i[WIDE ? 1 : 4][MAX_EXPERTS];
+  constexpr int NSEL = BIGK ? (WIDE ? 1 : 4) : 1;
+  __shared__ float sel_v[NSEL][BIGK ? MAX_EXPERTS : 1];
+  __shared__ int sel_i[NSEL][BIGK ? MAX_EXPERTS : 1];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -129,6 +133,8 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial,
     }
   }
 
+  float my_v = 0.f, l0 = 0.f;  // !BIGK: selection `lane`; the largest logit
+  int my_i = 0;
   for (int r = 0; r < k; ++r) {
     float bv = v[0];
     int bi = lane;
@@ -152,21 +158,35 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial,
       for (int j = 0; j < V; ++j)
         if (bi == lane + 64 * j) v[j] = -INFINITY;
     }
-    if (lane == 0) {
-      sel_v[sw][r] = bv;
-      sel_i[sw][r] = bi;
+    if (r == 0) l0 = bv;
+    if constexpr (BIGK) {
+      if (lane == 0) {
+        sel_v[sw][r] = bv;
+        sel_i[sw][r] = bi;
+      }
+    } else if (lane == r) {
+      my_v = bv;
+      my_i = bi;
     }
   }
   // weights: exp(L_j - L_0) / sum, the sum as a fixed butterfly
-  const float l0 = sel_v[sw][0];
   float psum = 0.f;
-  for (int r = lane; r < k; r += 64) psum += expf(sel_v[sw][r] - l0);
+  if constexpr (BIGK) {
+    for (int r = lane; r < k; r += 64) psum += expf(sel_v[sw][r] - l0);
+  } else {
+    if (lane < k) psum = expf(my_v - l0);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) psum += __shfl_xor(psum, off);
   const float inv = 1.0f / psum;
-  for (int r = lane; r < k; r += 64) {
-    ids[(int64_t)t * k + r] = sel_i[sw][r];
-    wout[(int64_t)t * k + r] = expf(sel_v[sw][r] - l0) * inv;
+  if constexpr (BIGK) {
+    for (int r = lane; r < k; r += 64) {
+      ids[(int64_t)t * k + r] = sel_i[sw][r];
+      wout[(int64_t)t * k + r] = expf(sel_v[sw][r] - l0) * inv;
+    }
+  } else if (lane < k) {
+    ids[(int64_t)t * k + lane] = my_i;
+    wout[(int64_t)t * k + lane] = expf(my_v - l0) * inv;
   }
 }
 
@@ -174,24 +194,43 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial,
 // workgroup per token
 constexpr int TOPK_WIDE_MAX_T = 1024;
 
+template <int V, bool WIDE>
+static void launch_topk_v(int grid, const float* partial, int nsplit, int64_t split_stride,
+                          const float* bias, int T, int E, int k, float* logits, int32_t* ids,
+                          float* w, hipStream_t st) {
+  if (k > 64)
+    hipLaunchKernelGGL((k_topk<V, WIDE, true>), dim3(grid), dim3(256), 0, st, partial, nsplit,
+                       split_stride, bias, T, E, k, logits, ids, w);
+  else
+    hipLaunchKernelGGL((k_topk<V, WIDE, false>), dim3(grid), dim3(256), 0, st, partial, nsplit,
+                       split_stride, bias, T, E, k, logits, ids, w);
+}
+
+template <int V>
+static void launch_topk_w(bool wide, const float* partial, int nsplit, int64_t split_stride,
+                          const float* bias, int T, int E, int k, float* logits, int32_t* ids,
+                          float* w, hipStream_t st) {
+  if (wide)
+    launch_topk_v<V, true>(T, partial, nsplit, split_stride, bias, T, E, k, logits, ids, w, st);
+  else
+    launch_topk_v<V, false>((T + 3) / 4, partial, nsplit, split_stride, bias, T, E, k, logits,
+                            ids, w, st);
+}
+
 hipError_t launch_topk(const float* partial, int nsplit, int64_t split_stride, const float* bias,
                        int T, int E, int k, float* logits, int32_t* ids, float* w, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const bool wide = T <= TOPK_WIDE_MAX_T;
-  const int grid = wide ? T : (T + 3) / 4;
-#define MOE_TOPK(V_)                                                                            \
-  if (wide)                                                                                     \
-    hipLaunchKernelGGL((k_topk<V_, true>), dim3(grid), dim3(256), 0, st, partial, nsplit,        \
-                       split_stride, bias, T, E, k, logits, ids, w);                             \
-  else                                                                                          \
-    hipLaunchKernelGGL((k_topk<V_, false>), dim3(grid), dim3(256), 0, st, partial, nsplit,       \
-                       split_stride, bias, T, E, k, logits, ids, w)
-  if (E <= 64) MOE_TOPK(1);
-  else if (E <= 128) MOE_TOPK(2);
-  else if (E <= 256) MOE_TOPK(4);
-  else if (E <= 512) MOE_TOPK(8);
-  else MOE_TOPK(16);
-#undef MOE_TOPK
+  if (E <= 64)
+    launch_topk_w<1>(wide, partial, nsplit, split_stride, bias, T, E, k, logits, ids, w, st);
+  else if (E <= 128)
+    launch_topk_w<2>(wide, partial, nsplit, split_stride, bias, T, E, k, logits, ids, w, st);
+  else if (E <= 256)
+    launch_topk_w<4>(wide, partial, nsplit, split_stride, bias, T, E, k, logits, ids, w, st);
+  else if (E <= 512)
+    launch_topk_w<8>(wide, partial, nsplit, split_stride, bias, T, E, k, logits, ids, w, st);
+  else
+    launch_topk_w<16>(wide, partial, nsplit, split_stride, bias, T, E, k, logits, ids, w, st);
   return hipGetLastError();
 }
 

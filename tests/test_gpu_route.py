@@ -25,6 +25,12 @@ CASES = [
     (1, 64, 1, 1, "f32", None),        # a single expert
     (9, 192, 33, 3, "f32", 1.0),
     (0, 128, 8, 2, "bf16", None),      # empty batch
+    # more than 1024 tokens: one wave per token
+    (1500, 256, 64, 8, "bf16", 1.0),
+    # k > 64: the selections go through LDS
+    (1200, 128, 128, 72, "bf16", None),
+    (40, 128, 200, 100, "f32", None),
+    (1100, 128, 1024, 70, "bf16", 0.5),
 ]
 
 
