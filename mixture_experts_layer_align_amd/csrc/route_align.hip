@@ -35,6 +35,37 @@ __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
 }
 
+// Wave-wide argmax under (value desc, index asc): afterwards every lane holds
+// the wave's best (value, index).  The first four levels pair lanes inside
+// each row of 16 with DPP moves (quad permutes xor 1 and xor 2, then the
+// half-row and row mirrors, which pair lanes of the two halves of the
+// previous level's groups); the last two cross rows with shuffles.  The
+// maximum of a total order does not depend on the pairing.
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float& bv, int& bi) {
+  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(bv), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_mov_dpp(bi, CTRL, 0xF, 0xF, false);
+  if (better(ov, oi, bv, bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+  argmax_dpp<0xB1>(bv, bi);   // quad_perm(1, 0, 3, 2): lane ^ 1
+  argmax_dpp<0x4E>(bv, bi);   // quad_perm(2, 3, 0, 1): lane ^ 2
+  argmax_dpp<0x141>(bv, bi);  // row_half_mirror: 7 - lane within 8
+  argmax_dpp<0x140>(bv, bi);  // row_mirror: 15 - lane within 16
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+}
+
 // Router partial planes are added in one fixed order whatever the launch
 // shape: four interleaved sums (planes q, q+4, q+8, ... in plane order, for
 // q = 0..3), then ((s0 + s1) + s2) + s3.  All V values of a plane are loaded
@@ -144,15 +175,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial,
         bv = v[j];
         bi = lane + 64 * j;
       }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    wave_argmax(bv, bi);
     if ((bi & 63) == lane) {
 #pragma unroll
       for (int j = 0; j < V; ++j)
@@ -414,6 +437,77 @@ __device__ void align_one_tile(const AlignArgs& a, const int32_t* ids, int* lds)
   write_layout(a, s_counts, s_off, sh);
 }
 
+// One wave aligns n <= 64 entries (ids in LDS, E <= 64 * EPL) without the
+// workgroup's histogram passes: lane i holds entry i, its rank among equal
+// entries below it comes from the match mask, the leader of each expert
+// writes the count to LDS, and lane l owns experts EPL*l .. EPL*l + EPL - 1
+// (contiguous, so one wave scan of the lanes' padded sums gives the offsets
+// in expert order).  Same layout as align_one_tile.  cl: E ints of LDS.
+template <int EPL>
+__device__ void align_one_wave(const AlignArgs& a, const int32_t* ids, int* cl) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.E, n = a.n, bm = a.bm;
+  const bool valid = lane < n;
+  const int e = valid ? ids[lane] : 0;
+  uint64_t mask = ballot(valid);
+  const int nbits = ilog2_ceil(E);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = ballot(valid && bit);
+    mask &= bit ? m : ~m;
+  }
+  const int rank = __popcll(mask & lanemask_lt());
+  for (int x = lane; x < E; x += 64) cl[x] = 0;
+  __builtin_amdgcn_wave_barrier();
+  if (valid && rank == 0) cl[e] = __popcll(mask);
+  __builtin_amdgcn_wave_barrier();
+  const int e0 = EPL * lane;
+  int c[EPL], pad[EPL], off[EPL];
+  int lsum = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    c[j] = e0 + j < E ? cl[e0 + j] : 0;
+    pad[j] = (c[j] + bm - 1) / bm * bm;
+    lsum += pad[j];
+  }
+  int inc = lsum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  const int total = __shfl(inc, 63);
+  int run = inc - lsum;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    off[j] = run;
+    run += pad[j];
+  }
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int ee = e0 + j;
+    if (ee >= E) continue;
+    a.counts[ee] = c[j];
+    a.offsets[ee] = off[j];
+    for (int s = off[j] + c[j]; s < off[j] + pad[j]; ++s) a.sorted_ids[s] = -1;
+    for (int b = off[j] / bm; b < (off[j] + pad[j]) / bm; ++b) a.block_expert[b] = ee;
+  }
+  if (lane == 0) a.offsets[E] = total;
+  for (int64_t s = total + lane; s < a.cap; s += 64) a.sorted_ids[s] = -1;
+  for (int64_t b = total / bm + lane; b < a.cap / bm; b += 64) a.block_expert[b] = -1;
+  // the entry's expert offset, from its owner lane
+  int oe = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int v = __shfl(off[j], e / EPL);
+    if (e % EPL == j) oe = v;
+  }
+  if (valid) {
+    a.sorted_ids[oe + rank] = lane;
+    a.inv_pos[lane] = oe + rank;
+  }
+}
+
 __global__ __launch_bounds__(AL_THREADS) void k_align_single(const AlignArgs a) {
   extern __shared__ int lds[];
   align_one_tile(a, a.ids, lds);
@@ -499,15 +593,7 @@ __global__ __launch_bounds__(AL_THREADS) void k_route_align_small(
           bv = v[j];
           bi = lane + 64 * j;
         }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
+      wave_argmax(bv, bi);
       if ((bi & 63) == lane) {
 #pragma unroll
         for (int j = 0; j < V; ++j)
@@ -531,7 +617,12 @@ __global__ __launch_bounds__(AL_THREADS) void k_route_align_small(
     }
   }
   __syncthreads();
-  align_one_tile(a, s_ids, al);
+  // up to 64 entries (and no tiled row list): one wave aligns them
+  if (a.n <= 64 && a.tile_rows == nullptr) {
+    if (wave == 0) align_one_wave<V>(a, s_ids, al);
+  } else {
+    align_one_tile(a, s_ids, al);
+  }
 }
 
 hipError_t launch_route_align_small(const float* partial, int nsplit, int64_t split_stride,
