@@ -93,6 +93,9 @@ typedef enum {
 #define MOE_BLOCK_M_MIN 16
 #define MOE_BLOCK_M_MAX 256
 #define MOE_MAX_EXPERTS 1024
+/* Routed entries T*k per call must stay below this (int32 slot indices with
+ * room for padding); larger calls return MOE_ERR_INVALID. */
+#define MOE_MAX_ENTRIES (1 << 24)
 
 /* Rows of the padded, expert-sorted buffer for T tokens, E experts, top-k and
  * block size bm: each active expert pads its count to a multiple of bm and at
@@ -115,7 +118,8 @@ int64_t moe_align_capacity(int T, int E, int k, int block_m);
  *   topk_w     [T, k]  fp32 out; softmax over E restricted to the selected
  *                      experts and renormalised to sum 1
  * Logits accumulate in fp32; the top-k decision is taken on those fp32 values.
- * Limits: 1 <= k <= E <= MOE_MAX_EXPERTS, d % 64 == 0, T >= 0.
+ * Limits: 1 <= k <= E <= MOE_MAX_EXPERTS, d % 64 == 0, T >= 0,
+ * T * k < MOE_MAX_ENTRIES.
  * ------------------------------------------------------------------------- */
 int moe_route(const void* x, const void* w_router, const float* logit_bias,
               int T, int d, int E, int k, int act_dtype,
@@ -139,7 +143,8 @@ int moe_route(const void* x, const void* w_router, const float* logit_bias,
  *   inv_pos        [T*k]  int32 out: the slot of entry t*k + j
  *   block_expert   [cap/block_m] int32 out: expert owning each block_m-row
  *                         block, -1 for blocks at or past padded_offsets[E]
- * block_m must be a power of two in [MOE_BLOCK_M_MIN, MOE_BLOCK_M_MAX].
+ * block_m must be a power of two in [MOE_BLOCK_M_MIN, MOE_BLOCK_M_MAX];
+ * 1 <= k <= E <= MOE_MAX_EXPERTS, T * k < MOE_MAX_ENTRIES (else MOE_ERR_INVALID).
  * No atomics decide the order: the result is unique and reproducible.
  * Out-of-range ids are a caller error (not checked on the device).
  * ------------------------------------------------------------------------- */
@@ -160,7 +165,7 @@ int moe_align(const int32_t* topk_ids, int T, int E, int k, int block_m,
 typedef struct {
   int d, d_ff, E, k;
   int act_dtype;                /* MOE_F32 or MOE_BF16: x, out, w_router      */
-  int w_dtype;                  /* MOE_F32, MOE_BF16 or MOE_FP8_E4M3         */
+  int w_dtype;                  /* MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 */
   const void* w_router;         /* [d, E] act_dtype                           */
   const float* logit_bias;      /* [E] fp32 or NULL                           */
   const void* w_gate_up;        /* [E, d, 2*d_ff]; cols [0,d_ff) gate,
@@ -203,7 +208,8 @@ typedef struct {
 
 /*   x    [T, d] act_dtype;  out [T, d] act_dtype (may not alias x).
  * Limits: 1 <= k <= E <= MOE_MAX_EXPERTS, d % 128 == 0, d_ff % 128 == 0,
- * T * k < 2^31, a supported dtype pair, FP8 scales present for FP8 weights. */
+ * T * k < MOE_MAX_ENTRIES, a supported dtype pair, FP8 / MXFP4 scales present
+ * for FP8 / MXFP4 weights. */
 int moe_forward(const moe_layer* layer, const void* x, int T, void* out,
                 void* workspace, size_t* workspace_bytes,
                 moe_routing_out* routing, void* stream);

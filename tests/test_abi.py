@@ -70,6 +70,8 @@ def test_route_validation_errors_before_any_launch():
     rc, need = _route(x=0, w=0, ids=0, tw=0)          # a query needs no data pointers
     assert rc == B.MOE_OK and need > 0          # workspace query
     assert _route(T=0, x=0, w=0, ids=0, tw=0)[0] == B.MOE_OK
+    # T*k at MOE_MAX_ENTRIES = 2^24 is rejected
+    assert _route(T=1 << 21, E=16, k=8)[0] == B.MOE_ERR_INVALID
 
 
 def test_align_validation_errors():
@@ -89,6 +91,10 @@ def test_align_validation_errors():
     n.value = 0
     assert lib.moe_align(None, 4, 8, 2, 32, p, p, p, p, p, vp(4096), ctypes.byref(n), None) \
         == B.MOE_ERR_INVALID                                        # data pointer missing
+    # routed entries T*k must stay below MOE_MAX_ENTRIES = 2^24
+    assert lib.moe_align(*args((1 << 21) - 1, 16, 8, 128)) == B.MOE_OK
+    assert lib.moe_align(*args(1 << 21, 16, 8, 128)) == B.MOE_ERR_INVALID
+    assert lib.moe_align(*args(1 << 24, 8, 1, 32)) == B.MOE_ERR_INVALID
 
 
 def _layer(**kw):

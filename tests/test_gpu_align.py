@@ -3,6 +3,8 @@ import numpy as np
 import pytest
 import torch
 
+import parity as P
+
 from mixture_experts_layer_align_amd import _binding as B
 from oracle import moe_oracle as O
 from workloads import make_topk_ids
@@ -18,6 +20,7 @@ CASES = [
     (3000, 1024, 3, 16, 0.7), (16384, 256, 8, 128, 1.2), (5000, 4, 1, 16, 30.0),
     (64, 32, 1, 32, 60.0),             # 64 entries on one expert: exact multiple of bm
     (1, 1024, 1, 256, None), (0, 8, 2, 32, None),
+    (20000, 1024, 8, 64, 1.0),         # every expert id, 40 tiles
 ]
 
 
@@ -42,3 +45,16 @@ def test_align_is_deterministic():
     b = B.align(ids, 256, 64)
     for key in a:
         assert torch.equal(a[key], b[key])
+
+
+def test_align_at_the_entry_limit():
+    # 16,777,208 entries, just below MOE_MAX_ENTRIES = 2^24 (4097 tiles);
+    # checked by the alignment's defining properties, which fix it uniquely
+    T, E, k, bm = (1 << 21) - 1, 16, 8, 128
+    ids = make_topk_ids(T, E, k, seed=13, skew=0.8)
+    print(f"align T={T} E={E} k={k} bm={bm}", flush=True)
+    got = B.align(ids.cuda(), E, bm)
+    torch.cuda.synchronize()
+    g = {key: v.cpu().numpy() for key, v in got.items()}
+    P.check_alignment_properties(ids.numpy(), E, bm, g["counts"], g["offsets"], g["sorted_ids"],
+                                 g["inv_pos"], g["block_expert"])

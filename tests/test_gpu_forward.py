@@ -86,6 +86,7 @@ SMALL = [
     (32, 8, 512, 256, "bf16", "mxfp4", 40, 1.2),
     (4, 2, 256, 512, "bf16", "mxfp4", 300, None),    # many rows per expert
     (16, 4, 768, 256, "bf16", "mxfp4", 257, 1.0),    # 24 scale blocks along d
+    (1024, 4, 256, 256, "bf16", "bf16", 300, None),  # MOE_MAX_EXPERTS experts
 ]
 
 
@@ -139,6 +140,21 @@ def test_forward_tiled_half_rows(E, k, d, d_ff, wdt, T, zipf):
     rem = rb["counts"].cpu().numpy() % 256
     assert ((rem > 0) & (rem <= 128)).any(), "no expert ends in a half row"
     assert (rem > 128).any(), "no expert ends in a partly filled full row"
+
+
+def test_forward_tiled_at_max_experts():
+    # 1024 experts with 64 routed rows each on average: the tiled GEMM, rows of
+    # every kind (empty experts, half rows, full rows); floats on a sample
+    sh = LayerShape(270, "max-experts", E=1024, k=4, d=512, d_ff=256, act="bf16", wdt="bf16",
+                    seed=71)
+    T = 16384
+    print(f"forward E=1024 k=4 d=512 d_ff=256 T={T}", flush=True)
+    layer = make_layer(sh, T, "cuda", zipf=0.8)
+    x = make_tokens(sh, T, "cuda")
+    rng = np.random.default_rng(270)
+    _, _, bm = run_and_check(layer, x, sample=np.sort(rng.choice(T, 48, replace=False)),
+                             what="max experts")
+    assert bm == 128
 
 
 def test_forward_is_deterministic():
