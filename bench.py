@@ -79,9 +79,9 @@ def main():
 
     from mixture_experts_layer_align_amd import _binding as B
     from mixture_experts_layer_align_amd import roofline as R
-    from workloads import CONFIGS, make_bias, make_layer, make_tokens
+    from workloads import LAYERS, make_bias, make_layer, make_tokens
 
-    sh = CONFIGS[args.config]
+    sh = LAYERS[args.config]
     decode_T = [t for t in sh.tokens if t <= 256]
     T = args.tokens if args.tokens is not None else (max(decode_T) if decode_T else max(sh.tokens))
     dev = torch.device("cuda:0")

@@ -26,7 +26,7 @@ Sources (the pages describe the computation, never a reference implementation):
     renormalise to sum 1) and the output formula sum_k w_k * SwiGLU_k(x) come
     from the workload statement, not from the pages.
 
-Readings where the sources are silent (each one is listed in the design doc):
+Readings where the sources are silent:
   R1 the logit bias is added before selection and before the softmax;
   R2 slot j holds the j-th largest logit, ties to the lower expert index;
   R3 the top-k decision is taken on logits rounded to the kernel's precision

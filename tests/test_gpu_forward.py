@@ -14,7 +14,7 @@ import torch
 import parity as P
 from mixture_experts_layer_align_amd import _binding as B
 from oracle import moe_oracle as O
-from workloads import CONFIGS, LayerShape, make_bias, make_layer, make_tokens
+from workloads import LAYERS, LayerShape, make_bias, make_layer, make_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -158,7 +158,7 @@ def test_forward_tiled_at_max_experts():
 
 
 def test_forward_is_deterministic():
-    sh = CONFIGS[3]
+    sh = LAYERS[3]
     layer = make_layer(sh, 256, "cuda")
     x = make_tokens(sh, 256, "cuda")
     fwd = B.Forward(layer.w_router, layer.bias, layer.w_gate_up, layer.w_down, sh.k)
@@ -170,15 +170,15 @@ def test_forward_is_deterministic():
 @functools.lru_cache(maxsize=1)
 def _config_layer(cfg):
     torch.cuda.empty_cache()
-    return make_layer(CONFIGS[cfg], None, "cuda", zipf=None)
+    return make_layer(LAYERS[cfg], None, "cuda", zipf=None)
 
 
-FULL = [(c, T) for c in sorted(CONFIGS) for T in CONFIGS[c].tokens]
+FULL = [(c, T) for c in sorted(LAYERS) for T in LAYERS[c].tokens]
 
 
 @pytest.mark.parametrize("cfg,T", FULL)
 def test_forward_benchmark_layers_full_size(cfg, T):
-    sh = CONFIGS[cfg]
+    sh = LAYERS[cfg]
     print(f"forward config {cfg} ({sh.name}) T={T}", flush=True)
     base = _config_layer(cfg)
     layer = dataclasses.replace(base, bias=make_bias(sh, sh.zipf_for(T), "cuda"))

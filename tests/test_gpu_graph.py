@@ -6,13 +6,13 @@ import pytest
 import torch
 
 from mixture_experts_layer_align_amd import _binding as B
-from workloads import CONFIGS, LayerShape, make_layer, make_tokens
+from workloads import LAYERS, LayerShape, make_layer, make_tokens
 
 pytestmark = pytest.mark.gpu
 
 CASES = [
     # (shape, T): decode stream path with split-K, fused routing; tiled path
-    (CONFIGS[1], 4),
+    (LAYERS[1], 4),
     (LayerShape(301, "graph-tiled", E=4, k=2, d=256, d_ff=256, act="bf16", wdt="bf16", seed=7),
      300),
     (LayerShape(302, "graph-mx", E=16, k=4, d=512, d_ff=256, act="bf16", wdt="mxfp4", seed=8),

@@ -296,8 +296,8 @@ def test_grouped_oracle_matches_bruteforce_loops(T, E, k, d, dff, bias):
 def test_tiny_fp32_layer_full_bruteforce():
     """The 16-token fp32 layer (E=8, top-2, d=128, d_ff=256) in full against the
     explicit loops."""
-    from workloads import CONFIGS, make_layer, make_tokens
-    sh = CONFIGS[0]
+    from workloads import LAYERS, make_layer, make_tokens
+    sh = LAYERS[0]
     lay = make_layer(sh, 16)
     x = O.decode_fp32(make_tokens(sh, 16).numpy())
     wr = O.decode_fp32(lay.w_router.numpy())

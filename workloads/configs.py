@@ -34,7 +34,7 @@ def _z(ts, s):
     return {t: s for t in ts}
 
 
-CONFIGS = {
+LAYERS = {
     0: LayerShape(0, "tiny-fp32", E=8, k=2, d=128, d_ff=256, act="f32", wdt="f32",
                   tokens=[16], zipf=_z([16], None), seed=0),
     1: LayerShape(1, "decode-bf16", E=8, k=2, d=4096, d_ff=14336, act="bf16", wdt="bf16",
@@ -47,7 +47,7 @@ CONFIGS = {
     4: LayerShape(4, "large-fp8-zipf1.2", E=256, k=8, d=7168, d_ff=2048, act="bf16",
                   wdt="fp8", tokens=[1, 16, 128, 16384], zipf=_z([1, 16, 128, 16384], 1.2),
                   seed=4),
-    # not one of the five benchmark layers: the layer of config 4 with MXFP4
+    # not one of the five benchmark layers: the E=256 top-8 fp8 layer with MXFP4
     # experts (the microscaling variant), decode batches only
     5: LayerShape(5, "large-mxfp4-zipf1.2", E=256, k=8, d=7168, d_ff=2048, act="bf16",
                   wdt="mxfp4", tokens=[1, 16, 128], zipf=_z([1, 16, 128], 1.2), seed=5),
@@ -55,4 +55,4 @@ CONFIGS = {
 
 
 def layer_shape(cfg: int) -> LayerShape:
-    return CONFIGS[cfg]
+    return LAYERS[cfg]
