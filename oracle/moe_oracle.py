@@ -132,6 +132,15 @@ def decode_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return vals * np.repeat(sc, MX_BLOCK, axis=0)[: 2 * K2]
 
 
+def decode_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """An MXFP8 matrix W[K, N] from its storage (reading R13): one e4m3fn code
+    per element, codes[k, n]; scales[k/32, n] the E8M0 scale shared by the
+    block of 32 consecutive k of column n.  W[k, n] = e4m3fn(code) * scale."""
+    codes = np.asarray(codes).astype(np.uint8)
+    K = codes.shape[0]
+    return decode_e4m3fn(codes) * np.repeat(decode_e8m0(scales), MX_BLOCK, axis=0)[:K]
+
+
 def decode(raw: np.ndarray, fmt: str) -> np.ndarray:
     if fmt == "bf16":
         return decode_bf16(raw)
@@ -266,14 +275,15 @@ def expert_weights_from_raw(w_gate_up, w_down, fmt: str, scale_gate_up=None,
     """Expert e's float64 (W_gate[d, d_ff], W_up[d, d_ff], W_down[d_ff, d]) from
     the stored arrays.  `w_gate_up[e]` is [d, 2*d_ff], gate columns first
     (reading R6); fp8 weights are decode(code) * scale per output column (R8);
-    MXFP4 weights are E2M1 codes times the E8M0 scale of their 32-element block
-    along K (R13).
+    MXFP4 and MXFP8 weights are E2M1 / e4m3fn codes times the E8M0 scale of
+    their 32-element block along K (R13).
     The arrays only need `[e]` indexing returning NumPy arrays, so experts can be
     fetched one at a time."""
     def fn(e: int):
-        if fmt == "mxfp4":
-            gu = decode_mxfp4(np.asarray(w_gate_up[e]), np.asarray(scale_gate_up[e]))
-            dn = decode_mxfp4(np.asarray(w_down[e]), np.asarray(scale_down[e]))
+        if fmt in ("mxfp4", "mxfp8"):
+            dec = decode_mxfp4 if fmt == "mxfp4" else decode_mxfp8
+            gu = dec(np.asarray(w_gate_up[e]), np.asarray(scale_gate_up[e]))
+            dn = dec(np.asarray(w_down[e]), np.asarray(scale_down[e]))
             dff = gu.shape[1] // 2
             return gu[:, :dff], gu[:, dff:], dn
         gu = decode(np.asarray(w_gate_up[e]), fmt)

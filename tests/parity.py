@@ -54,10 +54,13 @@ def oracle_layer(layer):
     wr = decode(layer.w_router)
     bias = None if layer.bias is None else layer.bias.detach().cpu().numpy().astype(np.float64)
     fmt = FMT[layer.w_gate_up.dtype]
+    if fmt == "fp8" and layer.scale_gate_up.dtype == torch.uint8:
+        fmt = "mxfp8"  # e4m3fn codes with E8M0 block scales
     sgu = sdn = None
-    if fmt in ("fp8", "mxfp4"):
-        sgu = _PerExpert(layer.scale_gate_up) if fmt == "mxfp4" else layer.scale_gate_up.cpu().numpy()
-        sdn = _PerExpert(layer.scale_down) if fmt == "mxfp4" else layer.scale_down.cpu().numpy()
+    if fmt in ("mxfp4", "mxfp8"):
+        sgu, sdn = _PerExpert(layer.scale_gate_up), _PerExpert(layer.scale_down)
+    elif fmt == "fp8":
+        sgu, sdn = layer.scale_gate_up.cpu().numpy(), layer.scale_down.cpu().numpy()
     fn = O.expert_weights_from_raw(_PerExpert(layer.w_gate_up), _PerExpert(layer.w_down), fmt,
                                    sgu, sdn)
     return wr, bias, fn

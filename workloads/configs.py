@@ -20,7 +20,7 @@ class LayerShape:
     d: int
     d_ff: int
     act: str            # "f32" | "bf16"   (x, out, router weight)
-    wdt: str            # "f32" | "bf16" | "fp8" | "mxfp4"  (expert weights)
+    wdt: str            # "f32" | "bf16" | "fp8" | "mxfp4" | "mxfp8"  (expert weights)
     tokens: List[int] = field(default_factory=list)
     # Zipf exponent of the router-logit bias per token count (None: no bias)
     zipf: Dict[int, Optional[float]] = field(default_factory=dict)

@@ -94,14 +94,30 @@ def quantize_mxfp4(w: torch.Tensor):
     return packed.contiguous(), (ex + 127.0).to(torch.uint8).contiguous()
 
 
+def quantize_mxfp8(w: torch.Tensor):
+    """w: [K, N] fp32 (K a multiple of 32) -> (codes [K, N] float8_e4m3fn,
+    scales [K/32, N] uint8).  Per block of 32 consecutive k of one column:
+    shared exponent floor(log2(max|w|)) - 8 (e4m3's largest binade is 2^8),
+    stored biased by 127 (E8M0); each element divided by 2^exponent, clamped
+    to +-448 (the largest e4m3fn magnitude) and rounded to the nearest e4m3fn
+    value (ties to even).  An all-zero block gets exponent 0 and zero codes."""
+    K, N = w.shape
+    blk = w.reshape(K // MX_BLOCK, MX_BLOCK, N)
+    amax = blk.abs().amax(dim=1)
+    ex = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, 1.0))) - 8.0,
+                     torch.zeros_like(amax)).clamp_(-127.0, 127.0)
+    x = (blk / torch.exp2(ex)[:, None, :]).reshape(K, N).clamp(-448.0, 448.0)
+    return x.to(torch.float8_e4m3fn).contiguous(), (ex + 127.0).to(torch.uint8).contiguous()
+
+
 @dataclass
 class Layer:
     shape: LayerShape
     w_router: torch.Tensor            # [d, E] act dtype
     w_gate_up: torch.Tensor           # [E, d, 2*d_ff] weight dtype (gate cols first)
     w_down: torch.Tensor              # [E, d_ff, d]
-    scale_gate_up: Optional[torch.Tensor]  # [E, 2*d_ff] fp32 (fp8 only)
-    scale_down: Optional[torch.Tensor]     # [E, d] fp32 (fp8 only)
+    scale_gate_up: Optional[torch.Tensor]  # fp8: [E, 2*d_ff] fp32; MX: [E, d/32, 2*d_ff] uint8
+    scale_down: Optional[torch.Tensor]     # fp8: [E, d] fp32; MX: [E, d_ff/32, d] uint8
     bias: Optional[torch.Tensor]      # [E] fp32 router-logit bias or None
 
     @property
@@ -138,6 +154,11 @@ def make_layer(shape: LayerShape, T: Optional[int] = None, device="cpu",
         wdn = torch.empty((E, dff // 2, d), dtype=torch.uint8, device=device)
         sgu = torch.empty((E, d // MX_BLOCK, 2 * dff), dtype=torch.uint8, device=device)
         sdn = torch.empty((E, dff // MX_BLOCK, d), dtype=torch.uint8, device=device)
+    elif shape.wdt == "mxfp8":
+        wgu = torch.empty((E, d, 2 * dff), dtype=torch.float8_e4m3fn, device=device)
+        wdn = torch.empty((E, dff, d), dtype=torch.float8_e4m3fn, device=device)
+        sgu = torch.empty((E, d // MX_BLOCK, 2 * dff), dtype=torch.uint8, device=device)
+        sdn = torch.empty((E, dff // MX_BLOCK, d), dtype=torch.uint8, device=device)
     elif shape.wdt == "fp8":
         wgu = torch.empty((E, d, 2 * dff), dtype=torch.float8_e4m3fn, device=device)
         wdn = torch.empty((E, dff, d), dtype=torch.float8_e4m3fn, device=device)
@@ -155,6 +176,9 @@ def make_layer(shape: LayerShape, T: Optional[int] = None, device="cpu",
         if shape.wdt == "mxfp4":
             wgu[e], sgu[e] = quantize_mxfp4(torch.cat([wg, wu], dim=1))
             wdn[e], sdn[e] = quantize_mxfp4(wd)
+        elif shape.wdt == "mxfp8":
+            wgu[e], sgu[e] = quantize_mxfp8(torch.cat([wg, wu], dim=1))
+            wdn[e], sdn[e] = quantize_mxfp8(wd)
         elif shape.wdt == "fp8":
             qg, sg = quantize_e4m3fn_per_column(wg)
             qu, su = quantize_e4m3fn_per_column(wu)
