@@ -185,7 +185,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "f32": "f32", "fp8": "bf16-act/fp8-weight",
-                  "mxfp4": "bf16-act/mxfp4-weight"}[sh.wdt],
+                  "mxfp4": "bf16-act/mxfp4-weight", "mxfp8": "bf16-act/mxfp8-weight"}[sh.wdt],
         "data": "synthetic",
         "config": {"workload": f"fused MoE layer forward, {sh.name}: E={sh.E} top-{sh.k} "
                                f"d={sh.d} d_ff={sh.d_ff} {sh.act} x / {sh.wdt} experts, T={T}",

@@ -71,11 +71,13 @@ typedef enum {
   MOE_F32 = 0,        /* IEEE binary32                                       */
   MOE_BF16 = 1,       /* bfloat16                                            */
   MOE_FP8_E4M3 = 2,   /* OCP FP8 E4M3 ("e4m3fn": max 448, no infinities)     */
-  MOE_MXFP4 = 3       /* OCP MX FP4: E2M1 codes + one E8M0 scale per 32 k    */
+  MOE_MXFP4 = 3,      /* OCP MX FP4: E2M1 codes + one E8M0 scale per 32 k    */
+  MOE_MXFP8 = 4       /* OCP MX FP8: e4m3fn codes + one E8M0 scale per 32 k  */
 } moe_dtype;
 
 /* Supported dtype combinations (activation / router weight, expert weight):
- * (F32, F32), (BF16, BF16), (BF16, FP8_E4M3), (BF16, MXFP4).  FP8 expert
+ * (F32, F32), (BF16, BF16), (BF16, FP8_E4M3), (BF16, MXFP4), (BF16, MXFP8).
+ * FP8 expert
  * weights carry one fp32 scale per expert and output column; the GEMM
  * multiplies its fp32 accumulator by that scale in the epilogue
  * (W = code * scale).
@@ -85,9 +87,12 @@ typedef enum {
  * k+1 in the high nibble), so an [K, N] weight is K/2 x N bytes; the E8M0
  * scale bytes s are [K/32, N].  E2M1 codes 0..7 are the magnitudes 0, 0.5, 1,
  * 1.5, 2, 3, 4, 6, code | 8 their negatives.  Scale bytes must lie in
- * [1, 254] (0 is read as a zero scale, 255 is not allowed).  The expert GEMMs
- * convert codes to bf16 exactly (scale applied in the conversion) and run the
- * bf16 MFMA; MXFP4 layers always take the weight-streaming GEMM.            */
+ * [1, 254] (0 is read as a zero scale, 255 is not allowed).
+ * MXFP8: W[k, n] = e4m3fn(code[k, n]) * 2^(s[k/32, n] - 127); one code byte
+ * per element ([K, N] like FP8), scale bytes [K/32, N] as for MXFP4.
+ * The expert GEMMs convert MX codes to bf16 exactly (scale applied in the
+ * conversion) and run the bf16 MFMA; MX layers always take the
+ * weight-streaming GEMM.                                                     */
 
 /* Allowed alignment block sizes (rows of one padded block). */
 #define MOE_BLOCK_M_MIN 16
@@ -165,17 +170,18 @@ int moe_align(const int32_t* topk_ids, int T, int E, int k, int block_m,
 typedef struct {
   int d, d_ff, E, k;
   int act_dtype;                /* MOE_F32 or MOE_BF16: x, out, w_router      */
-  int w_dtype;                  /* MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 */
+  int w_dtype;                  /* MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4,
+                                   MOE_MXFP8                                   */
   const void* w_router;         /* [d, E] act_dtype                           */
   const float* logit_bias;      /* [E] fp32 or NULL                           */
   const void* w_gate_up;        /* [E, d, 2*d_ff]; cols [0,d_ff) gate,
                                    [d_ff, 2*d_ff) up  (MXFP4: [E, d/2, 2*d_ff]
                                    bytes)                                      */
   const void* w_down;           /* [E, d_ff, d]  (MXFP4: [E, d_ff/2, d] bytes) */
-  const void* scale_gate_up;    /* FP8: [E, 2*d_ff] fp32; MXFP4: [E, d/32,
-                                   2*d_ff] E8M0 bytes; else NULL               */
-  const void* scale_down;       /* FP8: [E, d] fp32; MXFP4: [E, d_ff/32, d]
-                                   E8M0 bytes; else NULL                       */
+  const void* scale_gate_up;    /* FP8: [E, 2*d_ff] fp32; MXFP4 and MXFP8:
+                                   [E, d/32, 2*d_ff] E8M0 bytes; else NULL     */
+  const void* scale_down;       /* FP8: [E, d] fp32; MXFP4 and MXFP8:
+                                   [E, d_ff/32, d] E8M0 bytes; else NULL       */
 } moe_layer;
 
 /* Optional copies of the routing the forward computed.  Any pointer may be

@@ -14,7 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = 0, -1, -2, -3, -4
-MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8 = 0, 1, 2, 3, 4
 MOE_BLOCK_M_MAX = 256
 
 EXPORTED = ["moe_align_capacity", "moe_route", "moe_align", "moe_forward", "moe_forward_traced",
@@ -196,6 +196,9 @@ def make_layer_struct(w_router, bias, w_gate_up, w_down, k, scale_gate_up=None, 
     L.d, L.d_ff, L.E, L.k = d, two_dff // 2, E, k
     L.act_dtype = _ACT[w_router.dtype]
     L.w_dtype = _WDT[w_gate_up.dtype]
+    if L.w_dtype == MOE_FP8_E4M3 and scale_gate_up is not None and \
+            scale_gate_up.dtype == torch.uint8:
+        L.w_dtype = MOE_MXFP8  # e4m3fn codes with E8M0 block scales
     L.w_router, L.logit_bias = w_router.data_ptr(), (bias.data_ptr() if bias is not None else None)
     L.w_gate_up, L.w_down = w_gate_up.data_ptr(), w_down.data_ptr()
     L.scale_gate_up = scale_gate_up.data_ptr() if scale_gate_up is not None else None

@@ -87,6 +87,9 @@ struct DTr<W_FP4> {
   static constexpr int KSTEP = 32;  // = the MX block: one scale per column per k-step
   static constexpr int ESIZE = 1;   // (bytes per packed row pair and column)
 };
+// MXFP8: fp8's shape; one E8M0 scale per column per k-step (= the MX block)
+template <>
+struct DTr<W_MXFP8> : DTr<W_FP8> {};
 template <>
 struct DTr<W_F32> {
   static constexpr int CPL = 4;
@@ -103,7 +106,7 @@ struct DTr<W_F32> {
 // half their time waiting for loads).
 template <int WT>
 constexpr int stages_of() {
-  return WT == W_BF16 ? 2 : WT == W_FP4 ? 8 : 4;
+  return WT == W_BF16 ? 2 : WT == W_FP4 ? 8 : 4;  // fp8 and MXFP8: 4
 }
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
@@ -128,6 +131,12 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t src, float scale, i
   }
 }
 
+// Two e4m3fn codes (bytes 2*HI, 2*HI+1 of src) to two bf16, times `scale`.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t src, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, scale, HI));
+}
+
 __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
@@ -146,7 +155,8 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
   constexpr int ASZ = (ACT == ACT_BF16) ? 2 : 4;
   constexpr int XK = (ACT == ACT_BF16) ? 8 : 4;  // k-values per lane per token fragment
   constexpr int S = stages_of<WT>();
-  constexpr bool MX = WT == W_FP4;
+  constexpr bool MX = WT == W_FP4 || WT == W_MXFP8;  // E8M0 block scales
+  constexpr bool PACK = WT == W_FP4;                  // two codes per byte along K
   // vector-memory ops per stage: weight rows + 2 token loads (+ the MX scales)
   constexpr int PER = RPL + 2 + (MX ? 1 : 0);
   static_assert((S - 1) * PER <= 63, "vmcnt field");
@@ -189,14 +199,14 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
   }
   // the second slab of the last down tile may lie past the output width
   const bool active = (EPI != EPI_STORE) || (nt * 2 * SW + slab * SW < p.n_out);
-  // bytes between consecutive weight rows (MX: packed row pairs) and per k-step
+  // bytes between consecutive weight rows (MXFP4: packed row pairs) and per k-step
   const int64_t wrow_bytes = p.w_ld * Tr::ESIZE;
-  const int64_t kstep_bytes = (MX ? KSTEP / 2 : KSTEP) * wrow_bytes;
+  const int64_t kstep_bytes = (PACK ? KSTEP / 2 : KSTEP) * wrow_bytes;
   const int kb = split * p.kchunk;
   const int ke = min(p.K, kb + p.kchunk);
   const int nsteps = (ke - kb) / KSTEP;
   const char* wbase =
-      MX ? reinterpret_cast<const char*>(p.w) + (int64_t)e * (p.w_estride / 2) +
+      PACK ? reinterpret_cast<const char*>(p.w) + (int64_t)e * (p.w_estride / 2) +
                (int64_t)(kb / 2 + lg * RPL) * wrow_bytes + wcol
          : reinterpret_cast<const char*>(p.w) + (int64_t)e * p.w_estride * Tr::ESIZE +
                (int64_t)(kb + lg * RPL) * wrow_bytes + (int64_t)wcol * Tr::ESIZE;
@@ -265,13 +275,34 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
           if (q1) acc[1][c] = mfma_bf16_16x16x32(frag, x1, acc[1][c]);
         }
       } else {
+        // fp8 / MXFP8 codes, raw[j] = k-row j of the lane's 16 columns: a
+        // byte permute pairs the two consecutive-k bytes of two columns, and
+        // each pair converts to the column's bf16 operand word — with the
+        // column's E8M0 block scale for MXFP8 (exact: a power of two), 1 for
+        // fp8 (its per-column scale multiplies the fp32 sums later)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          u32x4 rows[8], frag[8];
+          u32x4 frag[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            rows[j] = fp8x8_to_bf16x8(half ? u32x2{raw[j][2], raw[j][3]} : u32x2{raw[j][0], raw[j][1]});
-          transpose8x8_b16(rows, frag);
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              const uint32_t a = raw[2 * m][2 * half + w], b = raw[2 * m + 1][2 * half + w];
+              const uint32_t u01 = __builtin_amdgcn_perm(b, a, 0x05010400u);  // cols 0, 1
+              const uint32_t u23 = __builtin_amdgcn_perm(b, a, 0x07030602u);  // cols 2, 3
+              // the lane's columns 8*half + 4*w + c; MXFP8: their E8M0 bytes,
+              // as the fp32 2^(e-127) (exponent field e, zero mantissa)
+              float scl[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+              if constexpr (WT == W_MXFP8) {
+                const uint32_t sw = mxs[s][2 * half + w];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) scl[c] = __uint_as_float(((sw >> (8 * c)) & 0xFFu) << 23);
+              }
+              frag[4 * w + 0][m] = fp8x2_to_bf16x2<false>(u01, scl[0]);
+              frag[4 * w + 1][m] = fp8x2_to_bf16x2<true>(u01, scl[1]);
+              frag[4 * w + 2][m] = fp8x2_to_bf16x2<false>(u23, scl[2]);
+              frag[4 * w + 3][m] = fp8x2_to_bf16x2<true>(u23, scl[3]);
+            }
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
             acc[0][8 * half + c] = mfma_bf16_16x16x32(frag[c], x0, acc[0][8 * half + c]);
@@ -468,10 +499,11 @@ hipError_t launch_splitk_silu(int act, const float* part, int nsplit, int64_t sp
 }
 
 int stream_tile_cols(int w_dtype, int epi) {
-  const int sw = 16 * (w_dtype == W_F32   ? DTr<W_F32>::CPL
-                       : w_dtype == W_FP8 ? DTr<W_FP8>::CPL
-                       : w_dtype == W_FP4 ? DTr<W_FP4>::CPL
-                                          : DTr<W_BF16>::CPL);
+  const int sw = 16 * (w_dtype == W_F32     ? DTr<W_F32>::CPL
+                       : w_dtype == W_FP8   ? DTr<W_FP8>::CPL
+                       : w_dtype == W_MXFP8 ? DTr<W_MXFP8>::CPL
+                       : w_dtype == W_FP4   ? DTr<W_FP4>::CPL
+                                            : DTr<W_BF16>::CPL);
   return epi == EPI_SILU_MUL ? sw : 2 * sw;
 }
 
@@ -500,6 +532,8 @@ hipError_t launch_stream_gemm(int act, int wdt, int epi, const StreamGemmArgs& a
   MOE_CASE(ACT_BF16, W_FP8, EPI_STORE)
   MOE_CASE(ACT_BF16, W_FP4, EPI_SILU_MUL)
   MOE_CASE(ACT_BF16, W_FP4, EPI_STORE)
+  MOE_CASE(ACT_BF16, W_MXFP8, EPI_SILU_MUL)
+  MOE_CASE(ACT_BF16, W_MXFP8, EPI_STORE)
 #undef MOE_CASE
   return hipErrorInvalidValue;
 }

@@ -49,7 +49,11 @@ struct Carve {
 
 int act_code(int dt) { return dt == MOE_BF16 ? ACT_BF16 : ACT_F32; }
 int w_code(int dt) {
-  return dt == MOE_FP8_E4M3 ? W_FP8 : dt == MOE_MXFP4 ? W_FP4 : dt == MOE_BF16 ? W_BF16 : W_F32;
+  return dt == MOE_FP8_E4M3 ? W_FP8
+         : dt == MOE_MXFP4  ? W_FP4
+         : dt == MOE_MXFP8  ? W_MXFP8
+         : dt == MOE_BF16   ? W_BF16
+                            : W_F32;
 }
 int act_bytes(int dt) { return dt == MOE_BF16 ? 2 : 4; }
 
@@ -333,14 +337,16 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   const bool pair_ok = (L->act_dtype == MOE_F32 && L->w_dtype == MOE_F32) ||
                        (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_BF16) ||
                        (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_FP8_E4M3) ||
-                       (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_MXFP4);
+                       (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_MXFP4) ||
+                       (L->act_dtype == MOE_BF16 && L->w_dtype == MOE_MXFP8);
   if (!pair_ok) return MOE_ERR_UNSUPPORTED;
   // fp8 and MXFP4 expert slabs are 256 columns wide
-  const bool scaled = L->w_dtype == MOE_FP8_E4M3 || L->w_dtype == MOE_MXFP4;
+  const bool scaled =
+      L->w_dtype == MOE_FP8_E4M3 || L->w_dtype == MOE_MXFP4 || L->w_dtype == MOE_MXFP8;
   if (scaled && (d % 256 != 0 || dff % 256 != 0)) return MOE_ERR_UNSUPPORTED;
   if (scaled && (L->scale_gate_up == nullptr || L->scale_down == nullptr))
     return MOE_ERR_INVALID;
-  const bool mx = L->w_dtype == MOE_MXFP4;
+  const bool mx = L->w_dtype == MOE_MXFP4 || L->w_dtype == MOE_MXFP8;
 
   const int act = act_code(L->act_dtype);
   const int wdt = w_code(L->w_dtype);

@@ -9,7 +9,7 @@ namespace moe {
 constexpr int MAX_EXPERTS = 1024;
 
 enum { ACT_F32 = 0, ACT_BF16 = 1 };             // activation storage
-enum { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_FP4 = 3 };  // expert-weight storage
+enum { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_FP4 = 3, W_MXFP8 = 4 };  // expert-weight storage
 // W_FP4: MXFP4 — E2M1 codes two per byte along K (even k in the low nibble),
 // one E8M0 scale byte per 32 consecutive k of a column (`scale` points to
 // bytes, scale_estride counts bytes).

@@ -52,10 +52,12 @@ def layer_work(T: int, d: int, d_ff: int, E: int, k: int, act: str, wdt: str,
     """`active` is the number of distinct experts the routing selected."""
     bx = ELEM_BYTES[act]
     rows = T * k
-    if wdt == "mxfp4":
-        # half a byte per weight, one E8M0 byte per 32 k of a column
-        w_gu = active * (d * 2 * d_ff // 2 + (d // 32) * 2 * d_ff)
-        w_dn = active * (d_ff * d // 2 + (d_ff // 32) * d)
+    if wdt in ("mxfp4", "mxfp8"):
+        # half a byte (MXFP4) or one byte (MXFP8) per weight, one E8M0 byte
+        # per 32 k of a column
+        num, den = (1, 2) if wdt == "mxfp4" else (1, 1)
+        w_gu = active * (d * 2 * d_ff * num // den + (d // 32) * 2 * d_ff)
+        w_dn = active * (d_ff * d * num // den + (d_ff // 32) * d)
     else:
         bw = ELEM_BYTES[wdt]
         scales_gu = active * 2 * d_ff * 4 if wdt == "fp8" else 0

@@ -163,12 +163,13 @@ def test_qk_norm_empty_work_enqueues_nothing():
     assert _qk(q=0, k=0, wq=0, wk=0, nq=0, nk=0) == B.MOE_OK
 
 
-def test_mxfp4_layer_validation():
-    # MXFP4 experts need bf16 activations, 256-wide d and d_ff, and both scales
+@pytest.mark.parametrize("wdt", [B.MOE_MXFP4, B.MOE_MXFP8])
+def test_mx_layer_validation(wdt):
+    # MX experts need bf16 activations, 256-wide d and d_ff, and both scales
     Bd = B
     layer = Bd.MoeLayer()
     layer.d, layer.d_ff, layer.E, layer.k = 256, 256, 8, 2
-    layer.act_dtype, layer.w_dtype = Bd.MOE_BF16, Bd.MOE_MXFP4
+    layer.act_dtype, layer.w_dtype = Bd.MOE_BF16, wdt
     layer.w_router = layer.w_gate_up = layer.w_down = 1
     lib = Bd.load()
     n = ctypes.c_size_t(0)

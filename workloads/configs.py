@@ -51,6 +51,9 @@ LAYERS = {
     # experts (the microscaling variant), decode batches only
     5: LayerShape(5, "large-mxfp4-zipf1.2", E=256, k=8, d=7168, d_ff=2048, act="bf16",
                   wdt="mxfp4", tokens=[1, 16, 128], zipf=_z([1, 16, 128], 1.2), seed=5),
+    # ... and with MXFP8 experts (e4m3fn codes, E8M0 block scales)
+    6: LayerShape(6, "large-mxfp8-zipf1.2", E=256, k=8, d=7168, d_ff=2048, act="bf16",
+                  wdt="mxfp8", tokens=[1, 16, 128], zipf=_z([1, 16, 128], 1.2), seed=6),
 }
 
 
