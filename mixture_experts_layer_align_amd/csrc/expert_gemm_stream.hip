@@ -46,9 +46,12 @@
 //     each output element adds k of them directly and a bf16 rounding there
 //     would stack on the output's own.
 //
-// fp8 (OCP e4m3fn) weights: a lane loads 16 codes of a row (slabs of 256
-// columns), converts them exactly to bf16 in registers and runs the same bf16
-// MFMA (activations stay bf16).  fp32 weights: 4 columns per lane, no
+// fp8 (OCP e4m3fn) and MXFP8 weights: a lane loads 16 codes of each of its 8
+// k-rows (slabs of 256 columns); byte permutes pair each column's codes of
+// two consecutive k-rows and one conversion per pair gives the column's bf16
+// operand word (MXFP8: scaled by the column's E8M0 block scale, exactly), so
+// no bf16 transpose is needed; the same bf16 MFMA runs (activations stay
+// bf16).  MXFP4: see its trait below.  fp32 weights: 4 columns per lane, no
 // transpose, v_mfma_f32_16x16x4_f32.
 #include <algorithm>
 #include <type_traits>
