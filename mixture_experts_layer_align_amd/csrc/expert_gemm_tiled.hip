@@ -257,6 +257,7 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
                                         int* next) {
   using C = Cfg<WT, HALF>;
   constexpr int S = C::STAGES;
+  static_assert(TILED_MIN_KCHUNK / TBK >= S + 2, "the pipeline needs nk > S (nk even)");
   constexpr int ESZ = C::ESZ;
   constexpr int CH = C::CHUNKS;    // 16-byte chunks per weight sub-tile row
   constexpr int EPC = 16 / ESZ;    // weight elements per chunk
@@ -387,12 +388,14 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
 
   // One k-step: MFMAs on `cur` (fp8: on the widened `wcur`); between them,
   // the reads of `nxt` from the stage at nxt_off (within the first 3/4 of the
-  // MFMAs, so they land before the step ends) and the direct loads of k-step
-  // refill_kt into stage refill_st.  Every op is pinned where it stands.
-  // FIRST: the accumulators start from zero.
-  auto step = [&](auto first_c, Frags<WT>& cur, const u32x4* wcur, Frags<WT>& nxt,
-                  uint32_t nxt_off, int refill_st, int refill_kt) __attribute__((always_inline)) {
+  // MFMAs, so they land before the step ends) and, with REFILL, the direct
+  // loads of k-step refill_kt into stage refill_st.  Every op is pinned where
+  // it stands.  FIRST: the accumulators start from zero.
+  auto step = [&](auto first_c, auto refill_c, Frags<WT>& cur, const u32x4* wcur,
+                  Frags<WT>& nxt, uint32_t nxt_off, int refill_st,
+                  int refill_kt) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_c)::value;
+    constexpr bool REFILL = decltype(refill_c)::value;
     static_for<NMFMA>([&](auto i_c) __attribute__((always_inline)) {
       constexpr int i = decltype(i_c)::value;
       constexpr int ni = i / MI, mi = i % MI;
@@ -409,10 +412,11 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
         if constexpr (slot_of(decltype(r_c)::value, C::NREAD, (3 * NMFMA) / 4) == i)
           read(r_c, nxt, nxt_off);
       });
-      static_for<C::DPT>([&](auto d_c) __attribute__((always_inline)) {
-        if constexpr (slot_of(decltype(d_c)::value, C::DPT, NMFMA) == i)
-          dma(d_c, refill_st, refill_kt);
-      });
+      if constexpr (REFILL)
+        static_for<C::DPT>([&](auto d_c) __attribute__((always_inline)) {
+          if constexpr (slot_of(decltype(d_c)::value, C::DPT, NMFMA) == i)
+            dma(d_c, refill_st, refill_kt);
+        });
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -420,14 +424,21 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
   // ---------------------------------------------------- main loop
   // The stage of k-step kt is kt % S.  At step kt, k-step kt+1 has landed
   // (waited for before the barrier) and every wave has finished reading stage
-  // kt%S (fragments kt were read and waited for in step kt-1), so that stage
-  // is refilled with k-step kt+S during the MFMAs while fragments kt+1 are
-  // read.  Every step has the same shape: past the end of K the refill
-  // reloads k-step kt (in bounds, never read again) and the last step's
-  // reads of the following stage are discarded, so S-1 k-steps of loads are
-  // always in flight.
+  // kt%S (fragments kt were read and waited for in step kt-1), so while
+  // fragments kt+1 are read during the MFMAs that stage is refilled with
+  // k-step kt+S — in the refill steps kt < nk-S.  In the last S steps fp8
+  // weights load nothing: at step kt the loads in flight are those of
+  // k-steps kt+1 .. min(kt+S-1, nk-1), so "k-step kt+1 landed" is a wait
+  // until the min(S-2, nk-2-kt) later k-steps' loads at most are
+  // outstanding, a constant in every step.  bf16 weights keep every step's
+  // shape there instead (the refill reloads k-step kt, in bounds, never read
+  // again, and the wait stays S-2): their registers are at the limit, and
+  // the loadless steps cost them a few spills that the saved loads did not
+  // pay back.  The last step's reads of the following stage are discarded.
+  // The launcher guarantees nk > S.
+  constexpr bool LOADLESS_TAIL = WT == W_FP8;
 #pragma unroll
-  for (int s = 0; s < S; ++s) dma_all(s, s < nk ? s : 0);
+  for (int s = 0; s < S; ++s) dma_all(s, s);
   Frags<WT> f0, f1;
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * C::DPT));
   __builtin_amdgcn_s_barrier();
@@ -435,23 +446,39 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
   wait_frags(f0);
   if constexpr (WT == W_FP8) widen_fp8(f0.b, w0);
 
-  auto one = [&](auto first_c, Frags<WT>& cur, const u32x4* wcur, Frags<WT>& nxt,
-                 u32x4* wnxt, int kt) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * C::DPT));
+  // LATER: k-steps' loads issued after those of kt+1 that may still be in
+  // flight; REFILL false: a tail step (fp8: no loads; bf16: reload k-step kt)
+  auto one = [&](auto first_c, auto refill_c, auto later_c, Frags<WT>& cur, const u32x4* wcur,
+                 Frags<WT>& nxt, u32x4* wnxt, int kt) __attribute__((always_inline)) {
+    constexpr bool REFILL = decltype(refill_c)::value;
+    constexpr int LATER = LOADLESS_TAIL ? decltype(later_c)::value : S - 2;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LATER * C::DPT));
     __builtin_amdgcn_s_barrier();
-    const int refill_kt = kt + S < nk ? kt + S : kt;
-    step(first_c, cur, wcur, nxt, lds_base + ((kt + 1) % S) * STB, kt % S, refill_kt);
+    step(first_c, std::integral_constant<bool, REFILL || !LOADLESS_TAIL>{}, cur, wcur, nxt,
+         lds_base + ((kt + 1) % S) * STB, kt % S, REFILL ? kt + S : kt);
     wait_frags(nxt);
     if constexpr (WT == W_FP8) widen_fp8(nxt.b, *reinterpret_cast<u32x4(*)[8]>(wnxt));
   };
-  // nk is even (a split is a multiple of 64 deep): step 0, pairs (1, 2) ... (nk-3, nk-2),
-  // then step nk-1
-  one(std::true_type{}, f0, w0, f1, w1, 0);
-  for (int kt = 1; kt + 1 < nk; kt += 2) {
-    one(std::false_type{}, f1, w1, f0, w0, kt);
-    one(std::false_type{}, f0, w0, f1, w1, kt + 1);
+  // nk and S are even (a split is a multiple of 64 deep): step 0, the refill
+  // pairs (1, 2) .. (nk-S-3, nk-S-2), step nk-S-1, then the S tail steps
+  // unrolled; fragments alternate f0 (even kt) / f1 (odd kt), so only f0 is
+  // live where the loop closes
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  one(T_{}, T_{}, IC<S - 2>{}, f0, w0, f1, w1, 0);
+  int kt = 1;
+  for (; kt + 1 < nk - S; kt += 2) {
+    one(F_{}, T_{}, IC<S - 2>{}, f1, w1, f0, w0, kt);
+    one(F_{}, T_{}, IC<S - 2>{}, f0, w0, f1, w1, kt + 1);
   }
-  one(std::false_type{}, f1, w1, f0, w0, nk - 1);
+  one(F_{}, T_{}, IC<S - 2>{}, f1, w1, f0, w0, kt);  // kt = nk-S-1
+  ++kt;
+  static_for<S / 2>([&](auto j_c) __attribute__((always_inline)) {
+    constexpr int j = decltype(j_c)::value;
+    constexpr int l0 = S - 2 - 2 * j, l1 = S - 3 - 2 * j;  // min(S-2, nk-2-kt)
+    one(F_{}, F_{}, IC<l0>{}, f0, w0, f1, w1, kt + 2 * j);
+    one(F_{}, F_{}, IC<(l1 > 0 ? l1 : 0)>{}, f1, w1, f0, w0, kt + 2 * j + 1);
+  });
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   // the last MFMAs' results are complete before anything else reads them
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -619,6 +646,9 @@ hipError_t launch_tiled_gemm(int epi, int w_dtype, int bm, const StreamGemmArgs&
       (epi == EPI_SILU_MUL && a.ksplit != 1))
     return hipErrorInvalidValue;
   if (bm == 128 && a.n_tiles % 2 != 0) return hipErrorInvalidValue;
+  // more k-steps per split than LDS stages (the pipeline's prologue fills
+  // every stage with real k-steps)
+  if (a.kchunk < TILED_MIN_KCHUNK) return hipErrorInvalidValue;
   if (a.tile_rows == nullptr || a.tile_counts == nullptr || a.die_next == nullptr)
     return hipErrorInvalidValue;
   // gate|up gathers tokens by slot, down reads its rows by slot

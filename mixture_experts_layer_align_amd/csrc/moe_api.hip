@@ -130,14 +130,15 @@ int choose_kchunk_balanced(int64_t items, int K, int kstep, int* nsplit, int bel
 // cost of each further fp32 output plane (written here and read again by the
 // combine, 8 bytes per routed row and output column at ~5.5 TB/s, against
 // 2*K flops per row and column at ~1.3 PFLOP/s: 945/K of the GEMM's ideal
-// time per plane).  Each split is a multiple of 64 deep; at most 4.
+// time per plane).  Each split is a multiple of 64 and at least
+// TILED_MIN_KCHUNK deep; at most 4.
 int choose_tiled_split(int64_t tiles, int K, int cus) {
   tiles = std::max<int64_t>(tiles, 1);
   const double ideal = (double)tiles / cus;
   int best = 1;
   double best_t = 1e30;
   for (int s = 1; s <= 4; ++s) {
-    if (K % (64 * s) != 0) continue;
+    if (K % (64 * s) != 0 || K / s < TILED_MIN_KCHUNK) continue;
     const double t = (double)((tiles * s + cus - 1) / cus) / s + (s - 1) * ideal * 945.0 / K;
     if (t < best_t * (1.0 - 1e-9)) {
       best_t = t;
@@ -356,7 +357,8 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   // (MXFP4 weights always take the weight-streaming GEMM)
   const bool tiled = act == ACT_BF16 && (wdt == W_BF16 || wdt == W_FP8) &&
                      n >= (int64_t)TILED_MIN_ROWS * E &&
-                     d % TILED_BN == 0 && dff % (TILED_BN / 2) == 0;
+                     d % TILED_BN == 0 && dff % (TILED_BN / 2) == 0 &&
+                     dff >= TILED_MIN_KCHUNK;
   // the tiled GEMM's half tiles pair two 256-column tiles, so experts are
   // padded to 128 rows when both GEMMs have an even number of column tiles
   const bool half_rows = tiled && (dff / (TILED_BN / 2)) % 2 == 0 && (d / TILED_BN) % 2 == 0;

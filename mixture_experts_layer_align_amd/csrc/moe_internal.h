@@ -85,11 +85,13 @@ hipError_t launch_splitk_silu(int act_dtype, const float* part, int nsplit, int6
 hipError_t launch_stream_gemm(int act_dtype, int w_dtype, int epi, const StreamGemmArgs& a,
                               hipStream_t st);
 
-// LDS-tiled MFMA grouped GEMM (thick blocks): bm-row blocks (256) x 256
-// weight columns, bf16 activations, bf16 or fp8 weights, K a multiple of 64;
-// EPI_SILU_MUL needs d_ff % 128 == 0, EPI_STORE needs n_out % 256 == 0.  No
-// k-split.
+// LDS-tiled MFMA grouped GEMM (thick blocks): tile rows of 256 (and 128
+// with bm = 128) x 256 weight columns, bf16 activations, bf16 or fp8
+// weights, K a multiple of 64; EPI_SILU_MUL needs d_ff % 128 == 0 and one
+// split, EPI_STORE n_out % 256 == 0; every split at least TILED_MIN_KCHUNK
+// deep (more k-steps than the kernel's LDS stages).
 constexpr int TILED_BN = 256;
+constexpr int TILED_MIN_KCHUNK = 256;
 hipError_t launch_tiled_gemm(int epi, int w_dtype, int bm, const StreamGemmArgs& a,
                              hipStream_t st);
 

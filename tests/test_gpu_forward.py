@@ -75,7 +75,8 @@ SMALL = [
     # >= 64 routed rows per expert and d % 256 == 0: the MFMA-tiled GEMM
     (4, 2, 256, 256, "bf16", "bf16", 300, None),
     (8, 2, 512, 384, "bf16", "bf16", 700, 1.2),      # skewed, ragged blocks
-    (1, 1, 256, 128, "bf16", "bf16", 200, None),     # one expert, 2 blocks
+    (1, 1, 256, 256, "bf16", "bf16", 200, None),     # one expert, 2 blocks
+    (1, 1, 256, 128, "bf16", "bf16", 200, None),     # d_ff too shallow to tile: streamed
     (16, 4, 768, 640, "bf16", "bf16", 1111, 0.8),
     # ... with fp8 weights (scales applied to the fp32 sums)
     (4, 2, 256, 512, "bf16", "fp8", 400, None),
@@ -110,7 +111,7 @@ def test_forward_all_tokens_on_one_expert_in_full_blocks(T):
     # a one-hot bias sends every token's slot 0 to expert 3; the tokens fill
     # whole blocks (two 32-row blocks of the streaming GEMM at T=64, four
     # 256-row blocks of the tiled GEMM at T=1024)
-    sh = LayerShape(250, "onehot", E=8, k=1, d=256, d_ff=128, act="bf16", wdt="bf16", seed=9)
+    sh = LayerShape(250, "onehot", E=8, k=1, d=256, d_ff=256, act="bf16", wdt="bf16", seed=9)
     layer = make_layer(sh, T, "cuda", zipf=None)
     bias = torch.zeros(8, dtype=torch.float32, device="cuda")
     bias[3] = 1e4
