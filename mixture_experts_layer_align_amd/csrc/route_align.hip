@@ -520,6 +520,49 @@ __global__ __launch_bounds__(AL_THREADS) void k_align_single(const AlignArgs a) 
 // lane registers; the ids also go to LDS, from where the workgroup aligns
 // them as k_align_single does.  One launch and one global round trip fewer.
 
+// Token t's top-k from its logits v (expert lane + 64j; -inf past E), as
+// k_topk selects them: k rounds of the wave argmax (value descending, index
+// ascending), selection r kept in lane r, weights exp(L_r - L_0) over their
+// sum.  Writes ids and weights, and the ids to s_ids.
+template <int V>
+__device__ __forceinline__ void select_topk(float (&v)[V], int lane, int t, int k,
+                                            int32_t* __restrict__ ids, float* __restrict__ wout,
+                                            int* s_ids) {
+  float myv = 0.f, l0 = 0.f;
+  int myi = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = v[0];
+    int bi = lane;
+#pragma unroll
+    for (int j = 1; j < V; ++j)
+      if (better(v[j], lane + 64 * j, bv, bi)) {
+        bv = v[j];
+        bi = lane + 64 * j;
+      }
+    wave_argmax(bv, bi);
+    if ((bi & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        if (bi == lane + 64 * j) v[j] = -INFINITY;
+    }
+    if (r == 0) l0 = bv;
+    if (lane == r) {
+      myv = bv;
+      myi = bi;
+    }
+  }
+  float psum = lane < k ? expf(myv - l0) : 0.f;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) psum += __shfl_xor(psum, off);
+  const float inv = 1.0f / psum;
+  if (lane < k) {
+    const int64_t o = (int64_t)t * k + lane;
+    ids[o] = myi;
+    wout[o] = expf(myv - l0) * inv;
+    s_ids[o] = myi;
+  }
+}
+
 // Plane loads in batches of NB planes (64 values a lane), each batch issued
 // before its adds (planes past nsplit reload the last plane and are not
 // added); sums in the order of plane_sums.
@@ -582,39 +625,7 @@ __global__ __launch_bounds__(AL_THREADS) void k_route_align_small(
         v[j] = -INFINITY;
       }
     }
-    float myv = 0.f, l0 = 0.f;
-    int myi = 0;
-    for (int r = 0; r < k; ++r) {
-      float bv = v[0];
-      int bi = lane;
-#pragma unroll
-      for (int j = 1; j < V; ++j)
-        if (better(v[j], lane + 64 * j, bv, bi)) {
-          bv = v[j];
-          bi = lane + 64 * j;
-        }
-      wave_argmax(bv, bi);
-      if ((bi & 63) == lane) {
-#pragma unroll
-        for (int j = 0; j < V; ++j)
-          if (bi == lane + 64 * j) v[j] = -INFINITY;
-      }
-      if (r == 0) l0 = bv;
-      if (lane == r) {
-        myv = bv;
-        myi = bi;
-      }
-    }
-    float psum = lane < k ? expf(myv - l0) : 0.f;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) psum += __shfl_xor(psum, off);
-    const float inv = 1.0f / psum;
-    if (lane < k) {
-      const int64_t o = (int64_t)t * k + lane;
-      ids[o] = myi;
-      wout[o] = expf(myv - l0) * inv;
-      s_ids[o] = myi;
-    }
+    select_topk<V>(v, lane, t, k, ids, wout, s_ids);
   }
   __syncthreads();
   // up to 64 entries (and no tiled row list): one wave aligns them

@@ -31,6 +31,12 @@ CASES = [
     (1200, 128, 128, 72, "bf16", None),
     (40, 128, 200, 100, "f32", None),
     (1100, 128, 1024, 70, "bf16", 0.5),
+    # a few tokens
+    (4, 2048, 128, 8, "bf16", 1.0),
+    (3, 1024, 256, 8, "bf16", 1.2),
+    (2, 4096, 8, 2, "f32", None),
+    (4, 512, 6, 6, "bf16", None),      # router rows not 16-byte aligned
+    (4, 256, 64, 64, "bf16", 0.5),     # k = E = 64
 ]
 
 
@@ -70,6 +76,21 @@ def test_route_exact_ties_go_to_lower_index():
     assert (pos[2] < pos[9]).all() and (pos[5] < pos[12]).all()
     lg = logits.cpu().numpy()
     assert (lg[:, 2] == lg[:, 9]).all()
+
+
+def test_route_exact_ties_go_to_lower_index_few_tokens():
+    # the same for a few tokens
+    sh = LayerShape(152, "route", E=16, k=4, d=256, d_ff=64, act="bf16", wdt="bf16", seed=79)
+    wr = make_router(sh, "cuda")
+    wr[:, 9] = wr[:, 2]
+    wr[:, 5] = wr[:, 12]
+    x = make_tokens(sh, 3, "cuda")
+    logits, ids, _ = B.route(x, wr, None, 16)
+    g = ids.cpu().numpy()
+    pos = {e: np.argmax(g == e, axis=1) for e in (2, 9, 5, 12)}
+    assert (pos[2] < pos[9]).all() and (pos[5] < pos[12]).all()
+    lg = logits.cpu().numpy()
+    assert (lg[:, 2] == lg[:, 9]).all() and (lg[:, 5] == lg[:, 12]).all()
 
 
 def test_route_is_deterministic():

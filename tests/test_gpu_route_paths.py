@@ -22,6 +22,9 @@ CASES = [
     (128, 8, 2048, 64, 1.0),
     (256, 8, 7168, 16, 1.2),
     (6, 6, 256, 9, None),        # k = E
+    (128, 8, 2048, 4, 1.0),
+    (6, 6, 256, 3, None),        # router rows not 16-byte aligned
+    (64, 64, 256, 4, 0.5),       # 256 entries: the workgroup aligns them
 ]
 
 
