@@ -11,7 +11,8 @@
 // because E need not be a multiple of the 16-byte chunk: columns past E are
 // read element by element and zero-filled.  A workgroup is two waves, each
 // streaming one 128-column slab (bf16; 64 for fp32) of its k-range for a block
-// of 32 tokens, with its loads running three k-steps ahead of its MFMAs.
+// of 32 tokens (when E fits one slab, the two waves share it and split the
+// k-range), with its loads running three k-steps ahead of its MFMAs.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -87,13 +88,25 @@ __global__ __launch_bounds__(128) void k_router_gemm(const StreamGemmArgs p) {
     arow[q] = reinterpret_cast<const char*>(p.a) + (int64_t)(rvalid[q] ? prow : 0) * p.a_ld * ASZ;
   }
   const bool use_q1 = ballot(rvalid[1]) != 0;
-  const int wcol = nt * 2 * SW + slab * SW + CPL * li;
-  const int ocol = nt * 2 * SW + slab * SW + lg * NV;
+  // E within one slab: both waves take that slab, wave 0 the first half of
+  // the split's k-steps and wave 1 the rest (its sums are added to wave 0's
+  // afterwards), instead of the second wave idling on columns past E
+  const bool kpair = p.n_tiles == 1 && p.n_out <= SW;
+  const int wslab = kpair ? 0 : slab;
+  const int wcol = nt * 2 * SW + wslab * SW + CPL * li;
+  const int ocol = nt * 2 * SW + wslab * SW + lg * NV;
   const char* w = reinterpret_cast<const char*>(p.w);
   const int64_t wrow_bytes = p.w_ld * Tr::ESIZE;
   const bool vec_ok = (p.w_ld % CPL) == 0;
-  const int kb = split * p.kchunk;
-  const int ke = min(p.K, kb + p.kchunk);
+  int kb = split * p.kchunk;
+  int ke = min(p.K, kb + p.kchunk);
+  if (kpair) {
+    const int half = ((ke - kb) / KSTEP + 1) / 2 * KSTEP;
+    if (slab == 0)
+      ke = kb + half;
+    else
+      kb += half;
+  }
 
   f32x4 acc[2][CPL];
 #pragma unroll
@@ -149,6 +162,26 @@ __global__ __launch_bounds__(128) void k_router_gemm(const StreamGemmArgs p) {
         if (it + d < nsteps) compute(d);
       }
     }
+  }
+  if (kpair) {
+    // wave 0's sums + wave 1's, in that order
+    __shared__ f32x4 xch[2][CPL][WAVE];
+    if (slab == 1) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) xch[q][c][lane] = acc[q][c];
+    }
+    __syncthreads();
+    if (slab == 1) return;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const f32x4 o = xch[q][c][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[q][c][r] += o[r];
+      }
   }
   // lane (li, lg) holds, for row group q, columns ocol + r*CPL + c in acc[q][c][r]
 #pragma unroll
