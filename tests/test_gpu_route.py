@@ -37,6 +37,10 @@ CASES = [
     (2, 4096, 8, 2, "f32", None),
     (4, 512, 6, 6, "bf16", None),      # router rows not 16-byte aligned
     (4, 256, 64, 64, "bf16", 0.5),     # k = E = 64
+    # E within one router slab: the workgroup's two waves split the k-steps,
+    # here odd counts per split (5, 3 + 2) and a short last split
+    (5, 320, 16, 4, "bf16", None),
+    (3, 704, 100, 5, "bf16", 1.0),
 ]
 
 
