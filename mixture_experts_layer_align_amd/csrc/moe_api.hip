@@ -17,6 +17,8 @@ constexpr int64_t WS_ALIGN = 256;
 // loads run 3 steps ahead).
 constexpr int ROUTER_TARGET_WGS = 1024;
 constexpr int ROUTER_MIN_STEPS = 4;
+// Token blocks up to which the router's tiles are one slab wide.
+constexpr int ROUTER_NARROW_MAX_BLOCKS = 8;
 // Expert GEMMs split K only when the blocks x n-tiles work items leave the chip
 // under-filled (fewer than SPLIT_BELOW two-wave workgroups); the split then
 // balances the compute units (choose_kchunk_balanced) and keeps at least
@@ -169,7 +171,10 @@ RouterPlan plan_router(const void* x, const void* w_router, int T, int d, int E,
   g.w_estride = 0;
   g.K = d;
   g.n_out = E;
-  const int tc = router_tile_cols(act);
+  // few token blocks: one-slab tiles, so twice the workgroups stream the
+  // router weight (its two waves split each tile's k-range)
+  const int tc = g.num_mblocks <= ROUTER_NARROW_MAX_BLOCKS ? router_slab_cols(act)
+                                                          : router_tile_cols(act);
   g.n_tiles = (E + tc - 1) / tc;
   g.kchunk = choose_kchunk((int64_t)g.num_mblocks * g.n_tiles, d, router_kstep(act), &g.ksplit,
                            ROUTER_TARGET_WGS, ROUTER_TARGET_WGS, ROUTER_MIN_STEPS,

@@ -98,6 +98,7 @@ hipError_t launch_tiled_gemm(int epi, int w_dtype, int bm, const StreamGemmArgs&
 // Router logits: A_DENSE rows, weights [K, n_out] with any n_out; split s writes
 // the fp32 plane out + s * out_split_stride.
 int router_tile_cols(int act_dtype);
+int router_slab_cols(int act_dtype);
 int router_kstep(int act_dtype);
 hipError_t launch_router_gemm(int act_dtype, const StreamGemmArgs& a, hipStream_t st);
 

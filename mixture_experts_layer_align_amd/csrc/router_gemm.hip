@@ -11,8 +11,9 @@
 // because E need not be a multiple of the 16-byte chunk: columns past E are
 // read element by element and zero-filled.  A workgroup is two waves, each
 // streaming one 128-column slab (bf16; 64 for fp32) of its k-range for a block
-// of 32 tokens (when E fits one slab, the two waves share it and split the
-// k-range), with its loads running three k-steps ahead of its MFMAs.
+// of 32 tokens (when E fits one slab, or few token blocks leave the chip
+// idle, a tile is one slab that the two waves share, splitting the k-range),
+// with its loads running three k-steps ahead of its MFMAs.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -88,13 +89,15 @@ __global__ __launch_bounds__(128) void k_router_gemm(const StreamGemmArgs p) {
     arow[q] = reinterpret_cast<const char*>(p.a) + (int64_t)(rvalid[q] ? prow : 0) * p.a_ld * ASZ;
   }
   const bool use_q1 = ballot(rvalid[1]) != 0;
-  // E within one slab: both waves take that slab, wave 0 the first half of
-  // the split's k-steps and wave 1 the rest (its sums are added to wave 0's
-  // afterwards), instead of the second wave idling on columns past E
-  const bool kpair = p.n_tiles == 1 && p.n_out <= SW;
-  const int wslab = kpair ? 0 : slab;
-  const int wcol = nt * 2 * SW + wslab * SW + CPL * li;
-  const int ocol = nt * 2 * SW + wslab * SW + lg * NV;
+  // One-slab tiles (n_tiles * SW >= E: E within one slab, or few token
+  // blocks, where the plan takes one slab per tile to run more workgroups):
+  // both waves take the tile's slab, wave 0 the first half of the split's
+  // k-steps and wave 1 the rest (its sums are added to wave 0's afterwards).
+  // Otherwise a tile is two slabs, one per wave.
+  const bool kpair = p.n_tiles * SW >= p.n_out;
+  const int tbase = kpair ? nt * SW : nt * 2 * SW + slab * SW;
+  const int wcol = tbase + CPL * li;
+  const int ocol = tbase + lg * NV;
   const char* w = reinterpret_cast<const char*>(p.w);
   const int64_t wrow_bytes = p.w_ld * Tr::ESIZE;
   const bool vec_ok = (p.w_ld % CPL) == 0;
@@ -200,6 +203,7 @@ __global__ __launch_bounds__(128) void k_router_gemm(const StreamGemmArgs p) {
 }
 
 int router_tile_cols(int act_dtype) { return act_dtype == ACT_BF16 ? 256 : 128; }
+int router_slab_cols(int act_dtype) { return router_tile_cols(act_dtype) / 2; }
 int router_kstep(int act_dtype) { return act_dtype == ACT_BF16 ? 32 : 16; }
 
 hipError_t launch_router_gemm(int act, const StreamGemmArgs& a, hipStream_t st) {
