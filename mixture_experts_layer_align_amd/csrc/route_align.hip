@@ -566,11 +566,11 @@ __device__ __forceinline__ void select_topk(float (&v)[V], int lane, int t, int 
 // Plane loads in batches of NB planes (64 values a lane), each batch issued
 // before its adds (planes past nsplit reload the last plane and are not
 // added); sums in the order of plane_sums.
-template <int V, int NSMAX>
+template <int V, int NSMAX, int NB_ = 0>
 __device__ __forceinline__ void plane_sums_all(const float* __restrict__ pp, int nsplit,
                                                int64_t split_stride, int E, int lane,
                                                float (&acc)[4][V]) {
-  constexpr int NB = (64 / V < NSMAX) ? 64 / V : NSMAX;
+  constexpr int NB = NB_ > 0 ? NB_ : (64 / V < NSMAX) ? 64 / V : NSMAX;
   static_assert(NB % 4 == 0 && NSMAX % NB == 0, "batches keep the plane order");
   int eo[V];
 #pragma unroll
@@ -598,8 +598,8 @@ __device__ __forceinline__ void plane_sums_all(const float* __restrict__ pp, int
   }
 }
 
-template <int V>
-__global__ __launch_bounds__(AL_THREADS) void k_route_align_small(
+template <int V, int NT>
+__global__ __launch_bounds__(NT) void k_route_align_small(
     const float* __restrict__ partial, int nsplit, int64_t split_stride,
     const float* __restrict__ bias, float* __restrict__ logits, int32_t* __restrict__ ids,
     float* __restrict__ wout, const AlignArgs a) {
@@ -609,10 +609,13 @@ __global__ __launch_bounds__(AL_THREADS) void k_route_align_small(
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int E = a.E, k = a.k;
-  for (int t = wave; t < a.T; t += AL_WAVES) {
+  // the narrow workgroup (fewer waves, more registers each) loads every
+  // plane in one batch: one memory round trip instead of two at V = 4
+  constexpr int NBS = NT < AL_THREADS ? ROUTER_MAX_SPLIT : 0;
+  for (int t = wave; t < a.T; t += NT / 64) {
     float acc[4][V];
-    plane_sums_all<V, ROUTER_MAX_SPLIT>(partial + (int64_t)t * E, nsplit, split_stride, E, lane,
-                                        acc);
+    plane_sums_all<V, ROUTER_MAX_SPLIT, NBS>(partial + (int64_t)t * E, nsplit, split_stride, E,
+                                             lane, acc);
     float v[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
@@ -628,11 +631,12 @@ __global__ __launch_bounds__(AL_THREADS) void k_route_align_small(
     select_topk<V>(v, lane, t, k, ids, wout, s_ids);
   }
   __syncthreads();
-  // up to 64 entries (and no tiled row list): one wave aligns them
-  if (a.n <= 64 && a.tile_rows == nullptr) {
+  // up to 64 entries (and no tiled row list): one wave aligns them (always
+  // so in the narrow workgroup)
+  if (NT < AL_THREADS || (a.n <= 64 && a.tile_rows == nullptr)) {
     if (wave == 0) align_one_wave<V>(a, s_ids, al);
   } else {
-    align_one_tile(a, s_ids, al);
+    if constexpr (NT == AL_THREADS) align_one_tile(a, s_ids, al);
   }
 }
 
@@ -643,19 +647,24 @@ hipError_t launch_route_align_small(const float* partial, int nsplit, int64_t sp
   if (!route_align_small_ok(a.T, a.E, a.k, nsplit)) return hipErrorInvalidValue;
   const size_t lds =
       ((size_t)a.n + (size_t)AL_WAVES * a.E + 2 * a.E + 1 + AL_WAVES + 1) * sizeof(int);
-#define MOE_RAS(V_)                                                                           \
+#define MOE_RAS(V_, NT_)                                                                      \
   do {                                                                                        \
     if (lds > 65536) {                                                                        \
-      hipError_t e_ = hipFuncSetAttribute((const void*)k_route_align_small<V_>,               \
+      hipError_t e_ = hipFuncSetAttribute((const void*)k_route_align_small<V_, NT_>,          \
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
       if (e_ != hipSuccess) return e_;                                                        \
     }                                                                                         \
-    hipLaunchKernelGGL((k_route_align_small<V_>), dim3(1), dim3(AL_THREADS), lds, st, partial, \
-                       nsplit, split_stride, bias, logits, ids, w, a);                             \
+    hipLaunchKernelGGL((k_route_align_small<V_, NT_>), dim3(1), dim3(NT_), lds, st, partial,  \
+                       nsplit, split_stride, bias, logits, ids, w, a);                          \
   } while (0)
-  if (a.E <= 64) MOE_RAS(1);
-  else if (a.E <= 128) MOE_RAS(2);
-  else MOE_RAS(4);
+  // more than 128 experts (4 logits a lane, planes loaded 16 at a time with
+  // 1024 threads), at most 8 tokens and 64 entries: 8 waves, all 32 planes
+  // in one batch
+  const bool narrow = a.E > 128 && a.T <= 8 && a.n <= 64 && a.tile_rows == nullptr;
+  if (a.E <= 64) MOE_RAS(1, AL_THREADS);
+  else if (a.E <= 128) MOE_RAS(2, AL_THREADS);
+  else if (narrow) MOE_RAS(4, 512);
+  else MOE_RAS(4, AL_THREADS);
 #undef MOE_RAS
   return hipGetLastError();
 }

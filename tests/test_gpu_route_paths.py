@@ -25,6 +25,9 @@ CASES = [
     (128, 8, 2048, 4, 1.0),
     (6, 6, 256, 3, None),        # router rows not 16-byte aligned
     (64, 64, 256, 4, 0.5),       # 256 entries: the workgroup aligns them
+    (256, 8, 7168, 4, 1.2),      # more than 128 experts, at most 8 tokens
+    (200, 8, 1024, 1, None),
+    (256, 8, 2048, 8, 1.0),
 ]
 
 
