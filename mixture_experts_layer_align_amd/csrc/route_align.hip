@@ -700,12 +700,32 @@ __global__ __launch_bounds__(AL_THREADS) void k_align_scatter(const AlignArgs a)
   int* s_tbase = s_off + E + 1;   // [E]
   int* sh = s_tbase + E;          // [AL_WAVES + 1]
   const int e = threadIdx.x;
+  // the tile's entries (ALIGN_TILE / AL_THREADS per thread), loaded before
+  // the histogram prefix they do not depend on
+  static_assert(ALIGN_TILE % AL_THREADS == 0, "entries per thread");
+  constexpr int EPT = ALIGN_TILE / AL_THREADS;
+  const int64_t i0 = (int64_t)blockIdx.x * ALIGN_TILE;
+  const int cntt = (int)min<int64_t>(ALIGN_TILE, a.n - i0);
+  int eid[EPT], erk[EPT];
+#pragma unroll
+  for (int u = 0; u < EPT; ++u) {
+    const int l = threadIdx.x + u * AL_THREADS;
+    eid[u] = l < cntt ? a.ids[i0 + l] : 0;
+    erk[u] = l < cntt ? a.rank[i0 + l] : 0;
+  }
   int cnt = 0, before = 0;
   if (e < E) {
-    for (int t = 0; t < a.ntiles; ++t) {
-      const int c = a.tile_hist[(int64_t)t * E + e];
-      if (t < (int)blockIdx.x) before += c;
-      cnt += c;
+    // sixteen tiles' counts in flight at a time (integer sums: any order)
+    for (int t0 = 0; t0 < a.ntiles; t0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        c[u] = t0 + u < a.ntiles ? a.tile_hist[(int64_t)(t0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (t0 + u < (int)blockIdx.x) before += c[u];
+        cnt += c[u];
+      }
     }
   }
   const int padded = (e < E) ? (cnt + a.bm - 1) / a.bm * a.bm : 0;
@@ -718,14 +738,15 @@ __global__ __launch_bounds__(AL_THREADS) void k_align_scatter(const AlignArgs a)
   }
   if (threadIdx.x == 0) s_off[E] = total;
   __syncthreads();
-  const int64_t i0 = (int64_t)blockIdx.x * ALIGN_TILE;
-  const int cntt = (int)min<int64_t>(ALIGN_TILE, a.n - i0);
-  for (int l = threadIdx.x; l < cntt; l += AL_THREADS) {
-    const int64_t i = i0 + l;
-    const int ee = a.ids[i];
-    const int pos = s_tbase[ee] + a.rank[i];
-    a.sorted_ids[pos] = (int)i;
-    a.inv_pos[i] = pos;
+#pragma unroll
+  for (int u = 0; u < EPT; ++u) {
+    const int l = threadIdx.x + u * AL_THREADS;
+    if (l < cntt) {
+      const int64_t i = i0 + l;
+      const int pos = s_tbase[eid[u]] + erk[u];
+      a.sorted_ids[pos] = (int)i;
+      a.inv_pos[i] = pos;
+    }
   }
   if (blockIdx.x == 0) write_layout(a, s_counts, s_off, sh);
 }
