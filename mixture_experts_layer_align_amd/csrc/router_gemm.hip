@@ -186,19 +186,31 @@ __global__ __launch_bounds__(128) void k_router_gemm(const StreamGemmArgs p) {
         for (int r = 0; r < 4; ++r) acc[q][c][r] += o[r];
       }
   }
-  // lane (li, lg) holds, for row group q, columns ocol + r*CPL + c in acc[q][c][r]
+  // lane (li, lg) holds, for row group q, columns ocol + r*CPL + c in acc[q][c][r]:
+  // CPL consecutive columns per r, stored 16 bytes at a time when rows are
+  // 16-byte aligned (E % 4 == 0) and the run lies within E
+  const bool vst = (p.out_ld % 4) == 0;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     if (!rvalid[q]) continue;
     float* dst = reinterpret_cast<float*>(p.out) + split * p.out_split_stride +
                  (int64_t)(p0 + 16 * q + li) * p.out_ld;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 4; ++r) {
+      const int col0 = ocol + r * CPL;
+      if (vst && col0 + CPL <= p.n_out) {
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int col = ocol + r * CPL + c;
-        if (col < p.n_out) dst[col] = acc[q][c][r];
+        for (int c4 = 0; c4 < CPL; c4 += 4) {
+          const u32x4 o = {__float_as_uint(acc[q][c4][r]), __float_as_uint(acc[q][c4 + 1][r]),
+                           __float_as_uint(acc[q][c4 + 2][r]), __float_as_uint(acc[q][c4 + 3][r])};
+          st16(dst + col0 + c4, o);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          if (col0 + c < p.n_out) dst[col0 + c] = acc[q][c][r];
       }
+    }
   }
 }
 
