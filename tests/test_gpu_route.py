@@ -41,6 +41,10 @@ CASES = [
     # here odd counts per split (5, 3 + 2) and a short last split
     (5, 320, 16, 4, "bf16", None),
     (3, 704, 100, 5, "bf16", 1.0),
+    # many token blocks and E not a multiple of 4 (partial planes stored one
+    # float at a time): a shared one-slab tile, and two-slab tiles
+    (600, 256, 37, 5, "bf16", 1.0),
+    (700, 128, 150, 6, "f32", 0.5),
 ]
 
 
