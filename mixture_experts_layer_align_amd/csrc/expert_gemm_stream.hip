@@ -146,8 +146,11 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
 
 }  // namespace
 
-// One item = (32-row block, n-tile, k-split) of the launch.
-template <int ACT, int WT, int EPI>
+// One item = (32-row block, n-tile, k-split) of the launch.  HILO: the token
+// rows come as bf16 pairs (p.a high halves, p.a_lo low halves) and every
+// weight fragment is applied to both, which carries h into the down GEMM at
+// 16 significant bits instead of 8.
+template <int ACT, int WT, int EPI, bool HILO>
 __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32x4* lds) {
   using Tr = DTr<WT>;
   constexpr int CPL = Tr::CPL;
@@ -160,8 +163,10 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
   constexpr int S = stages_of<WT>();
   constexpr bool MX = WT == W_FP4 || WT == W_MXFP8;  // E8M0 block scales
   constexpr bool PACK = WT == W_FP4;                  // two codes per byte along K
-  // vector-memory ops per stage: weight rows + 2 token loads (+ the MX scales)
-  constexpr int PER = RPL + 2 + (MX ? 1 : 0);
+  static_assert(!HILO || (ACT == ACT_BF16 && WT != W_F32), "bf16 pairs");
+  // vector-memory ops per stage: weight rows + 2 token loads (4 with HILO)
+  // (+ the MX scales)
+  constexpr int PER = RPL + (HILO ? 4 : 2) + (MX ? 1 : 0);
   static_assert((S - 1) * PER <= 63, "vmcnt field");
 
   const int lane = threadIdx.x & 63;
@@ -179,6 +184,7 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
 
   // -------------------------------------------------------- token rows
   const char* arow[2];
+  const char* alrow[2];  // HILO: the rows' low halves
   bool rvalid[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -188,6 +194,7 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
     int64_t src = 0;  // invalid rows read row 0 (in bounds) and are zeroed
     if (rvalid[q]) src = (p.a_mode == A_GATHER) ? sid / p.topk : prow;
     arow[q] = reinterpret_cast<const char*>(p.a) + src * p.a_ld * ASZ;
+    alrow[q] = HILO ? reinterpret_cast<const char*>(p.a_lo) + src * p.a_ld * ASZ : nullptr;
   }
   const bool use_q1 = ballot(rvalid[1]) != 0;
 
@@ -227,6 +234,7 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
 
   if (active && nsteps > 0) {
     u32x4 xb[S][2];
+    u32x4 xl[HILO ? S : 1][2];
     u32x4 mxs[MX ? S : 1];
     // stage s <- k-step `step` (clamped: steps past the end reload the last)
     auto issue = [&](int s, int step) {
@@ -237,6 +245,10 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
       const int64_t kk = (int64_t)(kb + sc * KSTEP + XK * lg) * ASZ;
       xb[s][0] = ld16(arow[0] + kk);
       xb[s][1] = ld16(arow[1] + kk);
+      if constexpr (HILO) {
+        xl[s][0] = ld16(alrow[0] + kk);
+        xl[s][1] = ld16(alrow[1] + kk);
+      }
       if constexpr (MX) mxs[s] = ld16(sbase + (int64_t)sc * p.w_ld);
     };
     // q1: the block's second 16-row group holds routed rows — a runtime bool
@@ -248,6 +260,24 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
       const u32x4 z = {0u, 0u, 0u, 0u};
       const u32x4 x0 = rvalid[0] ? xb[s][0] : z;
       const u32x4 x1 = rvalid[1] ? xb[s][1] : z;
+      const u32x4 x0l = (HILO && rvalid[0]) ? xl[HILO ? s : 0][0] : z;
+      const u32x4 x1l = (HILO && rvalid[1]) ? xl[HILO ? s : 0][1] : z;
+      // the 8 fragments' products with the high halves, then (HILO) with the
+      // low halves, so consecutive MFMAs use different accumulators
+      auto mm8 = [&](const u32x4 (&f)[8], int c0) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          acc[0][c0 + c] = mfma_bf16_16x16x32(f[c], x0, acc[0][c0 + c]);
+          if (q1) acc[1][c0 + c] = mfma_bf16_16x16x32(f[c], x1, acc[1][c0 + c]);
+        }
+        if constexpr (HILO) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            acc[0][c0 + c] = mfma_bf16_16x16x32(f[c], x0l, acc[0][c0 + c]);
+            if (q1) acc[1][c0 + c] = mfma_bf16_16x16x32(f[c], x1l, acc[1][c0 + c]);
+          }
+        }
+      };
       if constexpr (WT == W_F32) {
 #pragma unroll
         for (int ss = 0; ss < 4; ++ss)
@@ -260,22 +290,38 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
       } else if constexpr (WT == W_BF16) {
         u32x4 frag[8];
         transpose8x8_b16(raw, frag);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          acc[0][c] = mfma_bf16_16x16x32(frag[c], x0, acc[0][c]);
-          if (q1) acc[1][c] = mfma_bf16_16x16x32(frag[c], x1, acc[1][c]);
-        }
+        mm8(frag, 0);
       } else if constexpr (WT == W_FP4) {
+        // E8M0 byte e of column c -> the fp32 2^(e-127) (exponent field e,
+        // zero mantissa)
+        auto scl_of = [&](int c) {
+          return __uint_as_float(((mxs[s][c >> 2] >> (8 * (c & 3))) & 0xFFu) << 23);
+        };
+        if constexpr (!HILO) {
+          // one fragment at a time (fewest live registers)
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          // E8M0 byte e -> the fp32 2^(e-127) (exponent field e, zero mantissa)
-          const float scl = __uint_as_float(((mxs[s][c >> 2] >> (8 * (c & 3))) & 0xFFu) << 23);
-          u32x4 frag;
+          for (int c = 0; c < CPL; ++c) {
+            const float scl = scl_of(c);
+            u32x4 frag;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            frag[j] = fp4x2_to_bf16x2(raw[j][c >> 2], scl, c & 3);
-          acc[0][c] = mfma_bf16_16x16x32(frag, x0, acc[0][c]);
-          if (q1) acc[1][c] = mfma_bf16_16x16x32(frag, x1, acc[1][c]);
+            for (int j = 0; j < 4; ++j) frag[j] = fp4x2_to_bf16x2(raw[j][c >> 2], scl, c & 3);
+            acc[0][c] = mfma_bf16_16x16x32(frag, x0, acc[0][c]);
+            if (q1) acc[1][c] = mfma_bf16_16x16x32(frag, x1, acc[1][c]);
+          }
+        } else {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            u32x4 frag[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              const int cc = 8 * half + c;
+              const float scl = scl_of(cc);
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                frag[c][j] = fp4x2_to_bf16x2(raw[j][cc >> 2], scl, cc & 3);
+            }
+            mm8(frag, 8 * half);
+          }
         }
       } else {
         // fp8 / MXFP8 codes, raw[j] = k-row j of the lane's 16 columns: a
@@ -306,11 +352,7 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
               frag[4 * w + 2][m] = fp8x2_to_bf16x2<false>(u23, scl[2]);
               frag[4 * w + 3][m] = fp8x2_to_bf16x2<true>(u23, scl[3]);
             }
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            acc[0][8 * half + c] = mfma_bf16_16x16x32(frag[c], x0, acc[0][8 * half + c]);
-            if (q1) acc[1][8 * half + c] = mfma_bf16_16x16x32(frag[c], x1, acc[1][8 * half + c]);
-          }
+          mm8(frag, 8 * half);
         }
       }
     };
@@ -411,7 +453,11 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
       for (int r = 0; r < 4; ++r) h[r * CPL + c] = silu(g[r]) * u[r];
     }
     char* dst = reinterpret_cast<char*>(p.out) + (prow * p.out_ld + ocol) * ASZ;
-    store_act<ACT>(dst, h, NV);
+    if (ACT == ACT_BF16 && p.out_lo != nullptr)
+      store_bf16_pair<NV>(dst, reinterpret_cast<char*>(p.out_lo) + (prow * p.out_ld + ocol) * 2,
+                          h);
+    else
+      store_act<ACT>(dst, h, NV);
   } else {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -439,7 +485,7 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
 // front per expert group and no partly filled last round.  Items are numbered
 // n-tile fastest, so the blocks in use (a prefix of the m-blocks) make a
 // prefix of the items.
-template <int ACT, int WT, int EPI>
+template <int ACT, int WT, int EPI, bool HILO>
 __global__ __launch_bounds__(128) void k_expert_stream(const StreamGemmArgs p) {
   // ring[wave][stage][row][lane]; after an item's main loop the same memory
   // holds its epilogue exchange
@@ -449,7 +495,7 @@ __global__ __launch_bounds__(128) void k_expert_stream(const StreamGemmArgs p) {
   const int items = blocks * p.n_tiles * p.ksplit;
   for (int i = blockIdx.x; i < items; i += gridDim.x) {
     __syncthreads();  // the previous item's epilogue is done with the ring
-    stream_item<ACT, WT, EPI>(p, i, lds);
+    stream_item<ACT, WT, EPI, HILO>(p, i, lds);
   }
 }
 
@@ -459,7 +505,8 @@ template <int ACT>
 __global__ __launch_bounds__(256) void k_splitk_silu(const float* __restrict__ part, int nsplit,
                                                      int64_t split_stride, int64_t part_ld,
                                                      const int32_t* __restrict__ sorted_ids,
-                                                     int d_ff, char* __restrict__ h) {
+                                                     int d_ff, char* __restrict__ h,
+                                                     char* __restrict__ h_lo) {
   constexpr int ASZ = ACT == ACT_BF16 ? 2 : 4;
   const int64_t p = blockIdx.x;
   if (sorted_ids[p] < 0) return;
@@ -484,20 +531,25 @@ __global__ __launch_bounds__(256) void k_splitk_silu(const float* __restrict__ p
   float v[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = silu(g[j]) * u[j];
-  store_act<ACT>(h + (p * d_ff + n0) * ASZ, v, 8);
+  if (ACT == ACT_BF16 && h_lo != nullptr)
+    store_bf16_pair<8>(h + (p * d_ff + n0) * ASZ, h_lo + (p * d_ff + n0) * 2, v);
+  else
+    store_act<ACT>(h + (p * d_ff + n0) * ASZ, v, 8);
 }
 
 hipError_t launch_splitk_silu(int act, const float* part, int nsplit, int64_t split_stride,
                               int64_t part_ld, const int32_t* sorted_ids, int64_t rows, int d_ff,
-                              void* h, hipStream_t st) {
+                              void* h, void* h_lo, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   const dim3 grid((unsigned)rows, (unsigned)((d_ff + 2047) / 2048));
   if (act == ACT_BF16)
     hipLaunchKernelGGL(k_splitk_silu<ACT_BF16>, grid, dim3(256), 0, st, part, nsplit, split_stride,
-                       part_ld, sorted_ids, d_ff, reinterpret_cast<char*>(h));
+                       part_ld, sorted_ids, d_ff, reinterpret_cast<char*>(h),
+                       reinterpret_cast<char*>(h_lo));
   else
     hipLaunchKernelGGL(k_splitk_silu<ACT_F32>, grid, dim3(256), 0, st, part, nsplit, split_stride,
-                       part_ld, sorted_ids, d_ff, reinterpret_cast<char*>(h));
+                       part_ld, sorted_ids, d_ff, reinterpret_cast<char*>(h),
+                       reinterpret_cast<char*>(h_lo));
   return hipGetLastError();
 }
 
@@ -520,7 +572,17 @@ static hipError_t launch_one(const StreamGemmArgs& a, hipStream_t st) {
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFF || a.wgs < 0) return hipErrorInvalidValue;
   const int64_t grid = a.wgs > 0 ? std::min<int64_t>(a.wgs, items) : items;
-  hipLaunchKernelGGL((k_expert_stream<ACT, WT, EPI>), dim3((unsigned)grid), dim3(128), 0, st, a);
+  if constexpr (ACT == ACT_BF16 && WT != W_F32 && EPI == EPI_STORE) {
+    if (a.a_lo != nullptr) {
+      hipLaunchKernelGGL((k_expert_stream<ACT, WT, EPI, true>), dim3((unsigned)grid), dim3(128),
+                         0, st, a);
+      return hipGetLastError();
+    }
+  } else {
+    if (a.a_lo != nullptr) return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL((k_expert_stream<ACT, WT, EPI, false>), dim3((unsigned)grid), dim3(128), 0,
+                     st, a);
   return hipGetLastError();
 }
 

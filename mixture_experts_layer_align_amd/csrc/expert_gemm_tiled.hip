@@ -197,16 +197,63 @@ __device__ __forceinline__ void wait_frags(Frags<WT>& f) {
   for (int i = 0; i < MI; ++i) asm volatile("" : "+v"(f.a[i]));
 }
 
-// fp8 fragments widened to bf16 MFMA operands.  The widening is VALU work
-// feeding MFMAs the compiler cannot see, so the registers are tied to an
-// s_nop 1 after it: the two wait states a VALU write needs before an MFMA
-// reads the register.
+// fp8 fragments widened to bf16 (gate|up) or fp16 (down) MFMA operands, both
+// exact: every e4m3fn value is a bf16 and an fp16 normal.  The widening is
+// VALU work feeding MFMAs the compiler cannot see, so the registers are tied
+// to an s_nop 1 after it: the two wait states a VALU write needs before an
+// MFMA reads the register.
+template <bool F16>
 __device__ __forceinline__ void widen_fp8(const BRaw<W_FP8>& b, u32x4 (&op)[8]) {
 #pragma unroll
-  for (int ni = 0; ni < 8; ++ni) op[ni] = fp8x8_to_bf16x8(b.b8[ni]);
+  for (int ni = 0; ni < 8; ++ni) {
+    if constexpr (F16) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        op[ni][2 * h] = __builtin_bit_cast(
+            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.b8[ni][h], 1.0f, false));
+        op[ni][2 * h + 1] = __builtin_bit_cast(
+            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.b8[ni][h], 1.0f, true));
+      }
+    } else {
+      op[ni] = fp8x8_to_bf16x8(b.b8[ni]);
+    }
+  }
   asm volatile("s_nop 1"
                : "+v"(op[0]), "+v"(op[1]), "+v"(op[2]), "+v"(op[3]), "+v"(op[4]), "+v"(op[5]),
                  "+v"(op[6]), "+v"(op[7]));
+}
+
+// bf16 weight fragments rewritten in place as fp16 operands of the down
+// GEMM: each bf16 is widened to fp32 (its bits in the high half) and
+// converted with round toward zero, which is exact for magnitudes in fp16's
+// normal range [2^-14, 65504] (bf16 has 8 significant bits, fp16 11); smaller
+// ones lose at most 2^-24 as fp16 subnormals, larger ones saturate at 65504.
+// Same s_nop tie as widen_fp8.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t d) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(d << 16),
+                                                                 __uint_as_float(d & 0xFFFF0000u)));
+}
+__device__ __forceinline__ void widen_bf16_f16(BRaw<W_BF16>& b) {
+#pragma unroll
+  for (int ni = 0; ni < 8; ++ni)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      b.lo[ni][j] = bf16x2_to_f16x2(b.lo[ni][j]);
+      b.hi[ni][j] = bf16x2_to_f16x2(b.hi[ni][j]);
+    }
+  asm volatile("s_nop 1"
+               : "+v"(b.lo[0]), "+v"(b.lo[1]), "+v"(b.lo[2]), "+v"(b.lo[3]), "+v"(b.lo[4]),
+                 "+v"(b.lo[5]), "+v"(b.lo[6]), "+v"(b.lo[7]), "+v"(b.hi[0]), "+v"(b.hi[1]),
+                 "+v"(b.hi[2]), "+v"(b.hi[3]), "+v"(b.hi[4]), "+v"(b.hi[5]), "+v"(b.hi[6]),
+                 "+v"(b.hi[7]));
+}
+
+// h values as a pair of fp16, rounded to nearest even (|h| beyond 65504
+// overflows to infinity, which the output then shows).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // The k-loop MFMAs are inline assembly on accumulators pinned to AGPRs
@@ -219,11 +266,20 @@ __device__ __forceinline__ void widen_fp8(const BRaw<W_FP8>& b, u32x4 (&op)[8]) 
 // loop, operands written by VALU instructions are followed by s_nop padding
 // (widen_fp8), and s_nop padding separates the last MFMA from the epilogue's
 // reads.
+// F16: the fp16 form (the down GEMM), else bf16.
+template <bool F16>
 __device__ __forceinline__ void mfma_acc(f32x4& acc, const u32x4& a, const u32x4& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  if constexpr (F16)
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+template <bool F16>
 __device__ __forceinline__ void mfma_zero(f32x4& acc, const u32x4& a, const u32x4& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+  if constexpr (F16)
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
 }
 
 template <int I>
@@ -261,6 +317,9 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
   // gate|up's MFMAs compute the transposed blocks (weights as the first
   // operand; the two operands' lane layouts are the same) for its epilogue
   constexpr bool TRANSPOSED = EPI == EPI_SILU_MUL;
+  // the down GEMM runs on fp16 operands: h as the gate|up epilogue stored it
+  // (fp16, 11 significant bits) and the weights converted exactly
+  constexpr bool F16 = EPI == EPI_STORE;
   constexpr int ESZ = C::ESZ;
   constexpr int CH = C::CHUNKS;    // 16-byte chunks per weight sub-tile row
   constexpr int EPC = 16 / ESZ;    // weight elements per chunk
@@ -409,14 +468,14 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
         bf = u32x4{cur.b.lo[ni][0], cur.b.lo[ni][1], cur.b.hi[ni][0], cur.b.hi[ni][1]};
       if constexpr (FIRST)
         if constexpr (TRANSPOSED)
-          mfma_zero(acc[mi][ni], bf, cur.a[mi]);
+          mfma_zero<F16>(acc[mi][ni], bf, cur.a[mi]);
         else
-          mfma_zero(acc[mi][ni], cur.a[mi], bf);
+          mfma_zero<F16>(acc[mi][ni], cur.a[mi], bf);
       else
         if constexpr (TRANSPOSED)
-          mfma_acc(acc[mi][ni], bf, cur.a[mi]);
+          mfma_acc<F16>(acc[mi][ni], bf, cur.a[mi]);
         else
-          mfma_acc(acc[mi][ni], cur.a[mi], bf);
+          mfma_acc<F16>(acc[mi][ni], cur.a[mi], bf);
       static_for<C::NREAD>([&](auto r_c) __attribute__((always_inline)) {
         if constexpr (slot_of(decltype(r_c)::value, C::NREAD, (3 * NMFMA) / 4) == i)
           read(r_c, nxt, nxt_off);
@@ -453,7 +512,10 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
   __builtin_amdgcn_s_barrier();
   static_for<C::NREAD>([&](auto r) __attribute__((always_inline)) { read(r, f0, lds_base); });
   wait_frags(f0);
-  if constexpr (WT == W_FP8) widen_fp8(f0.b, w0);
+  if constexpr (WT == W_FP8)
+    widen_fp8<F16>(f0.b, w0);
+  else if constexpr (F16)
+    widen_bf16_f16(f0.b);
 
   // LATER: k-steps' loads issued after those of kt+1 that may still be in
   // flight; REFILL false: a tail step (fp8: no loads; bf16: reload k-step kt)
@@ -466,7 +528,10 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
     step(first_c, std::integral_constant<bool, REFILL || !LOADLESS_TAIL>{}, cur, wcur, nxt,
          lds_base + ((kt + 1) % S) * STB, kt % S, REFILL ? kt + S : kt);
     wait_frags(nxt);
-    if constexpr (WT == W_FP8) widen_fp8(nxt.b, *reinterpret_cast<u32x4(*)[8]>(wnxt));
+    if constexpr (WT == W_FP8)
+      widen_fp8<F16>(nxt.b, *reinterpret_cast<u32x4(*)[8]>(wnxt));
+    else if constexpr (F16)
+      widen_bf16_f16(nxt.b);
   };
   // nk and S are even (a split is a multiple of 64 deep): step 0, the refill
   // pairs (1, 2) .. (nk-S-3, nk-S-2), step nk-S-1, then the S tail steps
@@ -536,7 +601,8 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
           }
           hv[r] = silu(g) * u;
         }
-        const u32x2 o = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+        // h in fp16 for the down GEMM (see F16)
+        const u32x2 o = {pack_f16x2(hv[0], hv[1]), pack_f16x2(hv[2], hv[3])};
         *reinterpret_cast<u32x2*>(dst + ni * 16) = o;
       }
     }

@@ -424,7 +424,15 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   // tiled GEMM row list: at most one row per bm-block
   int32_t* trows = tiled ? c.take<int32_t>(2 * std::max<int64_t>(nblocks, 1)) : nullptr;
   int32_t* tcounts = tiled ? c.take<int32_t>(2 + TILE_COUNTERS) : nullptr;
+  // h; on the weight-streaming path with bf16 activations it is carried as a
+  // pair of bf16 planes (high halves, then low halves: 16 significant bits),
+  // whose second MFMA per weight fragment the decode GEMMs have issue slots
+  // for.  A single bf16 rounding of h measured up to 2.19e-2 * RMS on rows
+  // of the E=256 top-8 d=7168 layer (the bound is 2e-2), where the output's
+  // own rounding alone stays at 1.4e-2.
+  const bool h_pair = !tiled && act == ACT_BF16;
   char* h = c.take<char>(std::max<int64_t>(cap * dff * ab, 1));
+  char* h_lo = h_pair ? c.take<char>(std::max<int64_t>(cap * dff * 2, 1)) : nullptr;
   // per-slot expert outputs (fp32), or their k-split partial sums
   float* y = c.take<float>(std::max<int64_t>(dn_split * cap * d, 1));
   float* gu_part = gu_split > 1 ? c.take<float>(gu_split * cap * 2 * dff) : nullptr;
@@ -514,6 +522,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g.partial_ld = 2 * (int64_t)dff;
   g.partial_split_stride = cap * 2 * dff;
   g.out = h;
+  g.out_lo = h_lo;
   g.out_ld = dff;
   trace_mark(tr, &kidx, "gate_up", st);
   e = tiled ? launch_tiled_gemm(EPI_SILU_MUL, wdt, bm, g, st)
@@ -522,12 +531,13 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   if (gu_split > 1) {
     trace_mark(tr, &kidx, "gate_up_reduce", st);
     e = launch_splitk_silu(act, gu_part, gu_split, cap * 2 * dff, 2 * (int64_t)dff, sorted, cap,
-                           dff, h, st);
+                           dff, h, h_lo, st);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
   }
 
   StreamGemmArgs g2{};
   g2.a = h;
+  g2.a_lo = h_lo;
   g2.a_ld = dff;
   g2.a_mode = A_PADDED;
   g2.sorted_ids = sorted;

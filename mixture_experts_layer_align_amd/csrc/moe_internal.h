@@ -31,6 +31,8 @@ enum { EPI_SILU_MUL = 0,  // two slabs (gate, up) -> act dtype  h = silu(g)*u
 
 struct StreamGemmArgs {
   const void* a;          // row source
+  const void* a_lo;       // bf16 rows only: the low halves of rows carried as a pair of
+                          //   bf16 (value = a + a_lo, same layout), or NULL
   int64_t a_ld;           // elements
   int a_mode;
   const int32_t* sorted_ids;
@@ -54,6 +56,8 @@ struct StreamGemmArgs {
   int64_t partial_ld;     //   (columns in the weight's N space)
   int64_t partial_split_stride;
   void* out;
+  void* out_lo;           // EPI_SILU_MUL, bf16: also store h's low halves here
+                          //   (bf16(h - bf16(h)), layout of out), or NULL
   int64_t out_ld;
   int64_t out_split_stride;  // router: elements between split planes
   int wgs;                // stream GEMM: workgroups, each looping over items
@@ -79,9 +83,10 @@ int stream_kstep(int w_dtype);
 
 // h = SiLU(sum of gate partials) * (sum of up partials), splits in order, for
 // the rows whose slot holds a routed entry.
+// h_lo (bf16 only, or NULL): also store h's low halves, as out_lo above.
 hipError_t launch_splitk_silu(int act_dtype, const float* part, int nsplit, int64_t split_stride,
                               int64_t part_ld, const int32_t* sorted_ids, int64_t rows, int d_ff,
-                              void* h, hipStream_t st);
+                              void* h, void* h_lo, hipStream_t st);
 hipError_t launch_stream_gemm(int act_dtype, int w_dtype, int epi, const StreamGemmArgs& a,
                               hipStream_t st);
 

@@ -1,11 +1,12 @@
 // Routing (softmax / top-k / renormalisation) and expert alignment.
 //
 // Routing: one wave per token.  Each lane holds E/64 logits; k rounds of a
-// wave-wide butterfly argmax pick the slots in descending order with ties to
-// the lower index, and the renormalised softmax weight of slot j is
-// exp(L_j - L_max) / sum_j' exp(L_j' - L_max) (the softmax denominator over all
-// E cancels in the renormalisation).  The butterfly shuffles are the gfx950
-// form of the sub-warp horizontal reductions of "CuTeDSL at Perplexity"
+// wave-wide butterfly argmax over the experts not yet taken pick the slots
+// in descending order with ties to the lower index, and the renormalised
+// softmax weight of slot j is exp(L_j - L_max) / sum_j' exp(L_j' - L_max)
+// (the softmax denominator over all E cancels in the renormalisation).  The
+// butterfly shuffles are the gfx950 form of the sub-warp horizontal
+// reductions of "CuTeDSL at Perplexity"
 // (section on QK-norm, and the half-/quarter-warp reductions of its Blackwell
 // section).
 //
@@ -64,6 +65,39 @@ __device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
       bi = oi;
     }
   }
+}
+
+// One selection round over a wave's logits v (expert lane + 64j): the best
+// expert not yet taken, under (value desc, index asc), in every lane; its
+// owner lane marks it taken.  Taken experts are skipped rather than
+// overwritten, so logits of -inf (a masking bias) still rank by index after
+// the finite ones and no expert is selected twice.  Bits j of `taken` start
+// set for experts past E, which are never candidates; k <= E leaves an
+// untaken expert in every round.
+template <int V>
+__device__ __forceinline__ void pick_next(const float (&v)[V], uint32_t& taken, int lane,
+                                          float& bv, int& bi) {
+  static_assert(V <= 32, "taken mask");
+  bv = -INFINITY;
+  bi = 0x7FFFFFFF;  // no candidate: loses to any expert, -inf included
+#pragma unroll
+  for (int j = 0; j < V; ++j)
+    if (!((taken >> j) & 1u) && better(v[j], lane + 64 * j, bv, bi)) {
+      bv = v[j];
+      bi = lane + 64 * j;
+    }
+  wave_argmax(bv, bi);
+  if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+}
+
+// experts past E start out taken
+template <int V>
+__device__ __forceinline__ uint32_t taken_init(int lane, int E) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < V; ++j)
+    if (lane + 64 * j >= E) m |= 1u << j;
+  return m;
 }
 
 // Router partial planes are added in one fixed order whatever the launch
@@ -166,21 +200,11 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial,
 
   float my_v = 0.f, l0 = 0.f;  // !BIGK: selection `lane`; the largest logit
   int my_i = 0;
+  uint32_t taken = taken_init<V>(lane, E);
   for (int r = 0; r < k; ++r) {
-    float bv = v[0];
-    int bi = lane;
-#pragma unroll
-    for (int j = 1; j < V; ++j)
-      if (better(v[j], lane + 64 * j, bv, bi)) {
-        bv = v[j];
-        bi = lane + 64 * j;
-      }
-    wave_argmax(bv, bi);
-    if ((bi & 63) == lane) {
-#pragma unroll
-      for (int j = 0; j < V; ++j)
-        if (bi == lane + 64 * j) v[j] = -INFINITY;
-    }
+    float bv;
+    int bi;
+    pick_next<V>(v, taken, lane, bv, bi);
     if (r == 0) l0 = bv;
     if constexpr (BIGK) {
       if (lane == 0) {
@@ -520,31 +544,22 @@ __global__ __launch_bounds__(AL_THREADS) void k_align_single(const AlignArgs a) 
 // lane registers; the ids also go to LDS, from where the workgroup aligns
 // them as k_align_single does.  One launch and one global round trip fewer.
 
-// Token t's top-k from its logits v (expert lane + 64j; -inf past E), as
-// k_topk selects them: k rounds of the wave argmax (value descending, index
-// ascending), selection r kept in lane r, weights exp(L_r - L_0) over their
+// Token t's top-k from its logits v (expert lane + 64j; experts past E are
+// never candidates), as k_topk selects them: k rounds of the wave argmax
+// over the experts not yet taken (value descending, index ascending),
+// selection r kept in lane r, weights exp(L_r - L_0) over their
 // sum.  Writes ids and weights, and the ids to s_ids.
 template <int V>
-__device__ __forceinline__ void select_topk(float (&v)[V], int lane, int t, int k,
+__device__ __forceinline__ void select_topk(const float (&v)[V], int lane, int t, int E, int k,
                                             int32_t* __restrict__ ids, float* __restrict__ wout,
                                             int* s_ids) {
   float myv = 0.f, l0 = 0.f;
   int myi = 0;
+  uint32_t taken = taken_init<V>(lane, E);
   for (int r = 0; r < k; ++r) {
-    float bv = v[0];
-    int bi = lane;
-#pragma unroll
-    for (int j = 1; j < V; ++j)
-      if (better(v[j], lane + 64 * j, bv, bi)) {
-        bv = v[j];
-        bi = lane + 64 * j;
-      }
-    wave_argmax(bv, bi);
-    if ((bi & 63) == lane) {
-#pragma unroll
-      for (int j = 0; j < V; ++j)
-        if (bi == lane + 64 * j) v[j] = -INFINITY;
-    }
+    float bv;
+    int bi;
+    pick_next<V>(v, taken, lane, bv, bi);
     if (r == 0) l0 = bv;
     if (lane == r) {
       myv = bv;
@@ -628,7 +643,7 @@ __global__ __launch_bounds__(NT) void k_route_align_small(
         v[j] = -INFINITY;
       }
     }
-    select_topk<V>(v, lane, t, k, ids, wout, s_ids);
+    select_topk<V>(v, lane, t, E, k, ids, wout, s_ids);
   }
   __syncthreads();
   // up to 64 entries (and no tiled row list): one wave aligns them (always

@@ -1,9 +1,13 @@
 """moe_forward (the whole layer) against the oracle.
 
-Small layers run the oracle in full; the five benchmark layers run at their
-full sizes in the launch configuration the benchmark uses, with every integer
-output checked in full and the float output checked on all tokens (decode) or
-on a seeded sample of tokens (prefill)."""
+Routing is checked both ways (tests/parity.py): the oracle's top-k, weights
+and alignment on the GPU's own fp32 logits must match the GPU bit for bit on
+every token, and the GPU's logits must match the oracle's float64 logits.
+Float outputs are compared on every token of every layer, the
+full-size benchmark layers (up to 16,384 tokens of the E=256 top-8
+d=7168 layer) included, against the oracle's experts on the GPU's selection,
+with no token exempt.  The five benchmark layers run at full size in the
+launch configuration the benchmark uses."""
 import dataclasses
 import functools
 
@@ -18,8 +22,7 @@ from workloads import LAYERS, LayerShape, make_bias, make_layer, make_tokens
 
 pytestmark = pytest.mark.gpu
 
-
-def run_and_check(layer, x, sample=None, what=""):
+def run_and_check(layer, x, what=""):
     sh = layer.shape
     T = x.shape[0]
     fwd = B.Forward(layer.w_router, layer.bias, layer.w_gate_up, layer.w_down, sh.k,
@@ -31,31 +34,27 @@ def run_and_check(layer, x, sample=None, what=""):
         return out, rb, bm
     wr64, b64, efn = P.oracle_layer(layer)
     x64 = P.decode(x)
-    L64, oids, ow = O.route(x64, wr64, b64, sh.k)
-    # routing
-    P.assert_close_f32(rb["logits"].cpu().numpy(), L64, f"{what} logits")
+    glog = rb["logits"].cpu().numpy()
     gids = rb["topk_ids"].cpu().numpy()
-    ties = P.classify_ids(L64, gids, oids)
-    assert ties.size <= max(1, T // 100), f"{what}: {ties.size} near ties"
-    keep = np.setdiff1d(np.arange(T), ties)
-    P.assert_close_f32(rb["topk_w"].cpu().numpy()[keep], ow[keep], f"{what} topk_w")
-    # alignment
+    gw = rb["topk_w"].cpu().numpy()
     cap = O.capacity(T, sh.E, sh.k, bm)
     got = {k_: rb[k_].cpu().numpy() for k_ in ("counts", "offsets", "sorted_ids", "inv_pos")}
     got["sorted_ids"] = got["sorted_ids"][:cap]
     got["inv_pos"] = got["inv_pos"][:T * sh.k]
-    if ties.size == 0:
-        ref = O.align(oids, sh.E, bm)
-        for key in got:
-            assert (got[key] == ref[key]).all(), f"{what}: {key}"
-    else:
-        P.check_alignment_properties(gids, sh.E, bm, got["counts"], got["offsets"],
-                                     got["sorted_ids"], got["inv_pos"])
-    # output
-    rows = keep if sample is None else np.setdiff1d(sample, ties)
-    ref_out = O.outputs_for_tokens(x64, rows, oids, ow, efn)
-    o = P.decode(out)[rows]
-    P.assert_out_close(o, ref_out, sh.act, what)
+    # (i) boundary-fed: O2-O5 on the GPU's logits, bit-exact for every token
+    P.assert_boundary_fed(glog, gids, gw, sh.k, sh.E, bm, got, what)
+    # (ii) logits against O1; the oracle's own fp32 decision differs only at
+    # near ties within the logit tolerance (reported)
+    L64 = O.router_logits(x64, wr64, b64)
+    P.assert_close_f32(glog, L64, f"{what} logits")
+    ties = P.classify_ids(L64, gids, O.select_topk(L64.astype(np.float32), sh.k))
+    if ties.size:
+        print(f"{what}: {ties.size} near ties (GPU selection valid within the logit tolerance)")
+    w64 = O.topk_weights(L64, gids)
+    P.assert_close_f32(gw, w64, f"{what} topk_w (ii)")
+    # output of every token, on the GPU's selection
+    ref_out = O.outputs_for_tokens(x64, np.arange(T), gids, w64, efn)
+    P.assert_out_close(P.decode(out), ref_out, sh.act, f"{what} T={T}")
     return out, rb, bm
 
 
@@ -150,16 +149,14 @@ def test_forward_tiled_half_rows(E, k, d, d_ff, wdt, T, zipf):
 
 def test_forward_tiled_at_max_experts():
     # 1024 experts with 64 routed rows each on average: the tiled GEMM, rows of
-    # every kind (empty experts, half rows, full rows); floats on a sample
+    # every kind (empty experts, half rows, full rows)
     sh = LayerShape(270, "max-experts", E=1024, k=4, d=512, d_ff=256, act="bf16", wdt="bf16",
                     seed=71)
     T = 16384
     print(f"forward E=1024 k=4 d=512 d_ff=256 T={T}", flush=True)
     layer = make_layer(sh, T, "cuda", zipf=0.8)
     x = make_tokens(sh, T, "cuda")
-    rng = np.random.default_rng(270)
-    _, _, bm = run_and_check(layer, x, sample=np.sort(rng.choice(T, 48, replace=False)),
-                             what="max experts")
+    _, _, bm = run_and_check(layer, x, what="max experts")
     assert bm == 128
 
 
@@ -179,17 +176,7 @@ def _config_layer(cfg):
     return make_layer(LAYERS[cfg], None, "cuda", zipf=None)
 
 
-# The E=256 top-8 layer with MXFP8 experts at 128 tokens: one row (of 128) sits
-# at 2.19e-2 * RMS, past the 2e-2 bound.  A float64 emulation that rounds h and
-# the output to bf16 (the intermediates this layer keeps) gives the same error
-# on that row and its runners-up to four digits, so the excess is the bf16
-# rounding budget of the layer, not the kernel; kept as a strict expected
-# failure, so the suite notices if it ever changes.
-_ROUNDING_BUDGET = {(6, 128): "bf16 rounding of h and of the output alone exceeds 2e-2*RMS "
-                              "on one row (2.19e-2, identical in a float64 emulation)"}
-FULL = [pytest.param(c, T, marks=pytest.mark.xfail(strict=True, reason=_ROUNDING_BUDGET[(c, T)]))
-        if (c, T) in _ROUNDING_BUDGET else (c, T)
-        for c in sorted(LAYERS) for T in LAYERS[c].tokens]
+FULL = [(c, T) for c in sorted(LAYERS) for T in LAYERS[c].tokens]
 
 
 @pytest.mark.parametrize("cfg,T", FULL)
@@ -199,10 +186,4 @@ def test_forward_benchmark_layers_full_size(cfg, T):
     base = _config_layer(cfg)
     layer = dataclasses.replace(base, bias=make_bias(sh, sh.zipf_for(T), "cuda"))
     x = make_tokens(sh, T, "cuda")
-    sample = None
-    big = sh.d >= 7168  # the E=256 top-8 d=7168 layers (fp8, MXFP4, MXFP8 experts)
-    if T > (64 if big else 256):
-        # the float output on a seeded sample (every integer output in full)
-        rng = np.random.default_rng(cfg * 100003 + T)
-        sample = np.sort(rng.choice(T, size=24 if big else 48, replace=False))
-    run_and_check(layer, x, sample=sample, what=f"config {cfg} T={T}")
+    run_and_check(layer, x, what=f"config {cfg}")

@@ -1,6 +1,8 @@
 """moe_route (router logits, softmax, top-k, renormalisation) against the
-oracle: logits and weights within 1e-4*(1+|ref|); ids bit-exact except for
-near ties within that logit tolerance (counted, bounded)."""
+oracle: the oracle's top-k of the GPU's own fp32 logits equals the GPU's ids
+bit for bit (boundary-fed), logits and weights within 1e-4*(1+|ref|) of the
+float64 oracle, and where the oracle's own fp32 decision differs (a near tie)
+the GPU's choice is a valid top-k within that logit tolerance (reported)."""
 import numpy as np
 import pytest
 import torch
@@ -62,12 +64,13 @@ def test_route_matches_oracle(T, d, E, k, act, zipf):
         return
     b64 = None if bias is None else bias.cpu().numpy().astype(np.float64)
     L64, oids, ow = O.route(P.decode(x), P.decode(wr), b64, k)
-    P.assert_close_f32(logits.cpu().numpy(), L64, "logits")
     gids = ids.cpu().numpy()
+    P.assert_boundary_fed(logits.cpu().numpy(), gids, w.cpu().numpy(), k, what="route")
+    P.assert_close_f32(logits.cpu().numpy(), L64, "logits")
     ties = P.classify_ids(L64, gids, oids)
-    assert ties.size <= max(1, T // 100), f"{ties.size} near ties"
-    keep = np.setdiff1d(np.arange(T), ties)
-    P.assert_close_f32(w.cpu().numpy()[keep], ow[keep], "topk_w")
+    if ties.size:
+        print(f"{ties.size} near ties (GPU selection valid within the logit tolerance)")
+    P.assert_close_f32(w.cpu().numpy(), O.topk_weights(L64, gids), "topk_w")
     assert np.allclose(w.cpu().numpy().sum(axis=1), 1.0, atol=1e-6)
 
 
@@ -109,3 +112,51 @@ def test_route_is_deterministic():
     b = B.route(x, wr, None, 8)
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+MASKED = [
+    # T, E, k, finite experts: a -inf logit bias leaves fewer than k finite
+    # logits, so the last selections fall among the -inf experts (lowest ids
+    # first, each once) with weight 0
+    (3, 128, 8, 5),      # few tokens: the one-launch top-k + alignment
+    (40, 128, 8, 3),     # a workgroup per token
+    (1500, 64, 8, 6),    # a wave per token
+    (40, 200, 100, 30),  # k > 64: selections through LDS
+    (5, 256, 8, 1),      # E > 128 in the few-token path
+]
+
+
+@pytest.mark.parametrize("T,E,k,n_finite", MASKED)
+def test_route_masking_bias_fewer_finite_than_k(T, E, k, n_finite):
+    sh = LayerShape(160 + E, "route", E=E, k=k, d=256, d_ff=64, act="bf16", wdt="bf16",
+                    seed=3000 + T + n_finite)
+    wr = make_router(sh, "cuda")
+    x = make_tokens(sh, T, "cuda")
+    g = torch.Generator().manual_seed(T * 31 + E)
+    finite = torch.randperm(E, generator=g)[:n_finite]
+    bias = torch.full((E,), float("-inf"))
+    bias[finite] = torch.randn(n_finite, generator=g)
+    bias = bias.to("cuda")
+    print(f"masked route T={T} E={E} k={k} finite={n_finite}", flush=True)
+    logits, ids, w = B.route(x, wr, bias, k)
+    fwd = B.Forward(wr, bias, *_tiny_experts(E, 256), k)
+    rb = fwd.routing_buffers(T)
+    fwd(x, routing=rb)
+    torch.cuda.synchronize()
+    gl, gids, gw = logits.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+    assert np.isneginf(gl[:, np.setdiff1d(np.arange(E), finite.numpy())]).all()
+    P.assert_boundary_fed(gl, gids, gw, k, what="masked route")
+    for row in gids:
+        assert len(set(row.tolist())) == k, f"repeated expert {row}"
+    want = O.select_topk(gl, k)
+    assert (gids == want).all()
+    assert (gw[:, n_finite:] == 0).all() and np.allclose(gw.sum(axis=1), 1.0, atol=1e-6)
+    # the forward's own routing (few-token path for T <= 16) selects the same
+    assert (rb["topk_ids"].cpu().numpy() == gids).all()
+
+
+def _tiny_experts(E, d):
+    dff = 128
+    wgu = torch.zeros((E, d, 2 * dff), dtype=torch.bfloat16, device="cuda")
+    wdn = torch.zeros((E, dff, d), dtype=torch.bfloat16, device="cuda")
+    return wgu, wdn
