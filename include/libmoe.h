@@ -64,7 +64,9 @@ typedef enum {
   MOE_ERR_INVALID = -1,      /* NULL required pointer, bad size or range      */
   MOE_ERR_UNSUPPORTED = -2,  /* valid but not built: dtype mix, shape modulus */
   MOE_ERR_WORKSPACE = -3,    /* workspace smaller than required, or misaligned */
-  MOE_ERR_DEVICE = -4        /* the HIP runtime refused a launch or query     */
+  MOE_ERR_DEVICE = -4,       /* the HIP runtime refused a launch or query     */
+  MOE_ERR_SCRATCH = -5       /* moe_forward_noalloc: the call needs more than
+                                MOE_NOALLOC_SCRATCH_BYTES of scratch          */
 } moe_status;
 
 typedef enum {
@@ -223,6 +225,31 @@ int moe_forward(const moe_layer* layer, const void* x, int T, void* out,
 int moe_forward_traced(const moe_layer* layer, const void* x, int T, void* out,
                        void* workspace, size_t* workspace_bytes,
                        moe_routing_out* routing, moe_trace* trace, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_forward_noalloc — moe_forward for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, kernels and results as moe_forward, with
+ * the workspace taken from a static device array of MOE_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends.
+ *
+ *   Arguments as for moe_forward, without (workspace, workspace_bytes).  The
+ *   current device must be the device of `stream` and of every pointer.
+ *   A call whose workspace (moe_forward's query for the same layer and T)
+ *   exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_SCRATCH before
+ *   anything is enqueued; at 256 MiB this admits, e.g., every decode batch of
+ *   up to 64 tokens of an E=8 top-2 d=4096 d_ff=14336 layer and of up to 16
+ *   tokens of an E=256 top-8 d=7168 d_ff=2048 fp8 layer.  No allocation or
+ *   free of any kind happens in the call.  The array is set up on the first
+ *   call on each device (MOE_ERR_DEVICE if the runtime cannot resolve it).
+ *   All calls on one GPU share that GPU's array: calls that overlap in time
+ *   on one GPU (different streams, or host threads) race and corrupt each
+ *   other's results; serialise them.  The array's contents on entry do not
+ *   matter (nothing in it must start at zero).
+ * ------------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int moe_forward_noalloc(const moe_layer* layer, const void* x, int T, void* out,
+                        moe_routing_out* routing, void* stream);
 
 /* ---------------------------------------------------------------------------
  * moe_qk_norm — per-head RMS normalisation of query and key heads (QK-norm),

@@ -14,11 +14,13 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = 0, -1, -2, -3, -4
+MOE_ERR_SCRATCH = -5
+MOE_NOALLOC_SCRATCH_BYTES = 256 << 20
 MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8 = 0, 1, 2, 3, 4
 MOE_BLOCK_M_MAX = 256
 
 EXPORTED = ["moe_align_capacity", "moe_route", "moe_align", "moe_forward", "moe_forward_traced",
-            "moe_qk_norm", "moe_status_string", "moe_abi_version"]
+            "moe_forward_noalloc", "moe_qk_norm", "moe_status_string", "moe_abi_version"]
 
 _c = ctypes
 _vp = _c.c_void_p
@@ -76,6 +78,9 @@ def load():
     lib.moe_forward_traced.argtypes = [_c.POINTER(MoeLayer), _vp, _c.c_int, _vp, _vp,
                                        _c.POINTER(_c.c_size_t), _c.POINTER(MoeRoutingOut),
                                        _c.POINTER(MoeTrace), _vp]
+    lib.moe_forward_noalloc.restype = _c.c_int
+    lib.moe_forward_noalloc.argtypes = [_c.POINTER(MoeLayer), _vp, _c.c_int, _vp,
+                                        _c.POINTER(MoeRoutingOut), _vp]
     lib.moe_qk_norm.restype = _c.c_int
     lib.moe_qk_norm.argtypes = [_vp, _vp, _vp, _vp, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                 _c.c_int, _c.c_float, _c.c_float, _vp]
@@ -244,6 +249,34 @@ class Forward:
             "inv_pos": torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
         }
 
+    @staticmethod
+    def _routing_struct(routing, bm):
+        if routing is None:
+            return None
+        r = MoeRoutingOut()
+        r.logits = routing["logits"].data_ptr()
+        r.topk_ids = routing["topk_ids"].data_ptr()
+        r.topk_w = routing["topk_w"].data_ptr()
+        r.expert_counts = routing["counts"].data_ptr()
+        r.padded_offsets = routing["offsets"].data_ptr()
+        r.sorted_ids = routing["sorted_ids"].data_ptr()
+        r.inv_pos = routing["inv_pos"].data_ptr()
+        r.block_m = _c.pointer(bm)
+        return r
+
+    def noalloc(self, x: torch.Tensor, out: torch.Tensor, routing=None, stream=None):
+        """moe_forward_noalloc: the layer on x [T, d] into the caller's `out`,
+        with the library's static scratch instead of a workspace (raises
+        MoeError with MOE_ERR_SCRATCH when the batch needs more).  Returns
+        (out, block_m)."""
+        bm = _c.c_int(0)
+        r = self._routing_struct(routing, bm)
+        rc = self.lib.moe_forward_noalloc(_c.byref(self.L), _ptr(x), x.shape[0], _ptr(out),
+                                          _c.byref(r) if r is not None else None,
+                                          _stream(stream))
+        _check(rc, "moe_forward_noalloc")
+        return out, bm.value
+
     def __call__(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, routing=None,
                  events=None, stream=None):
         """Run the layer on x [T, d].  `routing`: dict from routing_buffers() to
@@ -255,17 +288,7 @@ class Forward:
         need = self._ensure_ws(T)
         nb = _c.c_size_t(need)
         bm = _c.c_int(0)
-        r = None
-        if routing is not None:
-            r = MoeRoutingOut()
-            r.logits = routing["logits"].data_ptr()
-            r.topk_ids = routing["topk_ids"].data_ptr()
-            r.topk_w = routing["topk_w"].data_ptr()
-            r.expert_counts = routing["counts"].data_ptr()
-            r.padded_offsets = routing["offsets"].data_ptr()
-            r.sorted_ids = routing["sorted_ids"].data_ptr()
-            r.inv_pos = routing["inv_pos"].data_ptr()
-            r.block_m = _c.pointer(bm)
+        r = self._routing_struct(routing, bm)
         rp = _c.byref(r) if r is not None else None
         if events is None:
             rc = self.lib.moe_forward(_c.byref(self.L), _ptr(x), T, _ptr(out), _ptr(self.ws),

@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/libmoe.h"
 #include "moe_internal.h"
@@ -223,6 +224,33 @@ int validate_route(int T, int d, int E, int k, int act) {
 
 }  // namespace
 
+// The no-allocation forward's workspace: one static device array, which every
+// GPU the library runs on holds (its own copy) until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: only the
+// address the runtime reports for the current device is ever used.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's copy of `scratch`, resolved on its first use there.
+int noalloc_scratch(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return MOE_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MOE_ERR_DEVICE;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
 namespace moe {
 int device_cus() {
   static int cached[64];
@@ -249,6 +277,7 @@ const char* moe_status_string(int s) {
     case MOE_ERR_UNSUPPORTED: return "unsupported dtype or shape";
     case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
     case MOE_ERR_DEVICE: return "HIP runtime error";
+    case MOE_ERR_SCRATCH: return "call needs more than the no-allocation scratch holds";
     default: return "unknown status";
   }
 }
@@ -581,6 +610,21 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
 int moe_forward(const moe_layer* L, const void* x, int T, void* out, void* workspace,
                 size_t* workspace_bytes, moe_routing_out* routing, void* stream) {
   return moe_forward_traced(L, x, T, out, workspace, workspace_bytes, routing, nullptr, stream);
+}
+
+int moe_forward_noalloc(const moe_layer* L, const void* x, int T, void* out,
+                        moe_routing_out* routing, void* stream) {
+  // the same validation and workspace plan as moe_forward (a query enqueues
+  // nothing)
+  size_t need = 0;
+  int rc = moe_forward(L, x, T, out, nullptr, &need, routing, stream);
+  if (rc != MOE_OK) return rc;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* ws = nullptr;
+  rc = noalloc_scratch(&ws);
+  if (rc != MOE_OK) return rc;
+  size_t have = MOE_NOALLOC_SCRATCH_BYTES;
+  return moe_forward(L, x, T, out, ws, &have, routing, stream);
 }
 
 }  // extern "C"

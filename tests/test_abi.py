@@ -35,7 +35,7 @@ def test_abi_version_and_status_strings():
     lib = B.load()
     assert lib.moe_abi_version() == 2
     for s in (B.MOE_OK, B.MOE_ERR_INVALID, B.MOE_ERR_UNSUPPORTED, B.MOE_ERR_WORKSPACE,
-              B.MOE_ERR_DEVICE):
+              B.MOE_ERR_DEVICE, B.MOE_ERR_SCRATCH):
         assert len(B.status_string(s)) > 0
 
 
@@ -181,3 +181,32 @@ def test_mx_layer_validation(wdt):
     assert q(layer) == Bd.MOE_ERR_UNSUPPORTED       # not a multiple of 256
     layer.d_ff, layer.act_dtype = 256, Bd.MOE_F32
     assert q(layer) == Bd.MOE_ERR_UNSUPPORTED       # fp32 activations
+
+
+def test_noalloc_refuses_a_batch_beyond_the_scratch():
+    # the E=256 top-8 d=7168 fp8 layer at 128 tokens needs ~319 MiB of
+    # workspace, more than the static scratch: refused on the host, before
+    # any pointer is used or anything is enqueued
+    L = B.MoeLayer()
+    L.d, L.d_ff, L.E, L.k = 7168, 2048, 256, 8
+    L.act_dtype, L.w_dtype = B.MOE_BF16, B.MOE_FP8_E4M3
+    L.w_router = L.w_gate_up = L.w_down = L.scale_gate_up = L.scale_down = 256
+    lib = B.load()
+    n = ctypes.c_size_t(0)
+    assert lib.moe_forward(ctypes.byref(L), None, 128, None, None, ctypes.byref(n), None,
+                           None) == B.MOE_OK
+    assert n.value > B.MOE_NOALLOC_SCRATCH_BYTES
+    rc = lib.moe_forward_noalloc(ctypes.byref(L), ctypes.c_void_p(256), 128,
+                                 ctypes.c_void_p(512), None, None)
+    assert rc == B.MOE_ERR_SCRATCH
+    assert "scratch" in B.status_string(rc)
+    # invalid shapes fail validation first, as for moe_forward
+    L.k = 0
+    assert lib.moe_forward_noalloc(ctypes.byref(L), ctypes.c_void_p(256), 128,
+                                   ctypes.c_void_p(512), None, None) == B.MOE_ERR_INVALID
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(os.path.join(ROOT, "include", "libmoe.h")).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.MOE_NOALLOC_SCRATCH_BYTES
