@@ -257,6 +257,7 @@ def main():
     }
     if not args.only and not args.no_qk:
         line["qk_norm"] = qk_norm_bench(B, R, dev, args.steps)
+        line["rms_norm"] = rms_norm_bench(B, R, dev, args.steps)
     if args.copy_calibration:
         # a plain copy of known size, so hardware byte counters can be scaled
         n = args.copy_calibration * (1 << 20)
@@ -299,6 +300,40 @@ def qk_norm_bench(B, roof, dev, steps):
     us = t0.elapsed_time(t1) * 1e3 / n
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"workload": f"QK-norm in place, bf16, T={T}, {nq} q + {nk} k heads of {hd}",
+            "us_per_launch": us, "algorithmic_bytes_per_launch": nbytes, "GB/s": gbs,
+            "frac_of_hbm_peak": gbs * 1e9 / roof.HBM_BYTES_PER_S, "cache_guard_copies": copies}
+
+
+def rms_norm_bench(B, roof, dev, steps):
+    """Row RMSNorm of an 8192-token batch at the E=256 top-8 layer's hidden
+    size (d = 7168, bf16), out of place: HBM-bound, algorithmic bytes = x read
+    once, y written once (+ the gain).  Launches cycle through copies of x and
+    y so that one cycle moves >= 1 GiB (Infinity-Cache guard)."""
+    import torch
+    from workloads.norm import make_rows
+    T, d = 8192, 7168
+    nbytes = 2 * T * d * 2 + d * 2
+    copies = max(1, min(MAX_REPLICAS, -(-GUARD_BYTES // nbytes)))
+    sets = []
+    for i in range(copies):
+        x, g = make_rows(T, d, "bf16", seed=i, device=dev)
+        sets.append((x, g, torch.empty_like(x)))
+    for i in range(max(3, copies)):
+        x, g, y = sets[i % copies]
+        B.rms_norm(x, g, out=y, eps=1e-6)
+    torch.cuda.synchronize()
+    n = max(steps, 20) * copies
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(n):
+        x, g, y = sets[i % copies]
+        B.rms_norm(x, g, out=y, eps=1e-6)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / n
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": f"row RMSNorm, bf16, T={T}, d={d}, out of place",
             "us_per_launch": us, "algorithmic_bytes_per_launch": nbytes, "GB/s": gbs,
             "frac_of_hbm_peak": gbs * 1e9 / roof.HBM_BYTES_PER_S, "cache_guard_copies": copies}
 

@@ -260,14 +260,37 @@ int moe_forward_noalloc(const moe_layer* layer, const void* x, int T, void* out,
                         moe_routing_out* routing, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_rms_norm — row RMS normalisation over the hidden size (RMSNorm).
+ * "La fusion de noyaux", section 4.2, reduction + elementwise: for every row
+ * t of x,
+ *   out[t, i] = x[t, i] / sqrt(sum_j x[t, j]^2 / d + eps) * (weight[i] + weight_bias),
+ * in one pass (x read once, out written once), sums in fp32, rounded once to
+ * the element type.  weight_bias is the constant some models add to the gain
+ * ("CuTeDSL at Perplexity", RMS-norm remarks); 0 gives the plain formula.
+ *
+ *   x       [T, d]  dtype
+ *   weight  [d]     dtype (the gain g)
+ *   out     [T, d]  dtype; may be x itself (in place), must not otherwise
+ *                   overlap it
+ *   dtype   MOE_BF16 or MOE_F32
+ * Limits: T >= 0, d * element size a multiple of 16 bytes and at most 32 KiB
+ * (bf16: d % 8 == 0, d <= 16384; fp32: d % 4 == 0, d <= 8192; else
+ * MOE_ERR_UNSUPPORTED), eps >= 0 and finite, weight_bias finite (else
+ * MOE_ERR_INVALID).  No workspace.
+ * ------------------------------------------------------------------------- */
+int moe_rms_norm(const void* x, const void* weight, void* out, int T, int d, int dtype,
+                 float weight_bias, float eps, void* stream);
+
+/* ---------------------------------------------------------------------------
  * moe_qk_norm — per-head RMS normalisation of query and key heads (QK-norm),
  * in place.  "CuTeDSL at Perplexity", section on the RMS-norm kernel
- * specialised for small dimensions: for every token t and every head of q
- * (then of k), with x the head's head_dim values and w the tensor's weight,
- *   x <- (w + weight_bias) * x * rsqrt(sum(x * x) / head_dim + eps),
+ * specialised for small dimensions: the norm above applied to every head of
+ * q (with q_weight) and of k (with k_weight) of every token, over the head's
+ * head_dim values:
+ *   x <- x * rsqrt(sum(x * x) / head_dim + eps) * (w + weight_bias),
  * rounded once to the element type.  (The section's one-line formula omits
- * the reciprocal square root its kernel listing applies; the listing is
- * followed.)
+ * the reciprocal square root; its kernel applies one, as does the RMSNorm of
+ * "La fusion de noyaux".)
  *
  *   q         [T, n_q_heads, head_dim]  dtype, read and overwritten
  *   k         [T, n_k_heads, head_dim]  dtype, read and overwritten

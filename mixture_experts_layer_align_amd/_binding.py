@@ -20,7 +20,8 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8 = 0, 1, 2, 3, 4
 MOE_BLOCK_M_MAX = 256
 
 EXPORTED = ["moe_align_capacity", "moe_route", "moe_align", "moe_forward", "moe_forward_traced",
-            "moe_forward_noalloc", "moe_qk_norm", "moe_status_string", "moe_abi_version"]
+            "moe_forward_noalloc", "moe_rms_norm", "moe_qk_norm", "moe_status_string",
+            "moe_abi_version"]
 
 _c = ctypes
 _vp = _c.c_void_p
@@ -81,6 +82,9 @@ def load():
     lib.moe_forward_noalloc.restype = _c.c_int
     lib.moe_forward_noalloc.argtypes = [_c.POINTER(MoeLayer), _vp, _c.c_int, _vp,
                                         _c.POINTER(MoeRoutingOut), _vp]
+    lib.moe_rms_norm.restype = _c.c_int
+    lib.moe_rms_norm.argtypes = [_vp, _vp, _vp, _c.c_int, _c.c_int, _c.c_int, _c.c_float,
+                                 _c.c_float, _vp]
     lib.moe_qk_norm.restype = _c.c_int
     lib.moe_qk_norm.argtypes = [_vp, _vp, _vp, _vp, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                 _c.c_int, _c.c_float, _c.c_float, _vp]
@@ -170,6 +174,21 @@ def align(topk_ids: torch.Tensor, E: int, block_m: int, stream=None):
                              _ptr(out["block_expert"]), ws, nb, _stream(stream))
     ws, nb = _workspace(call, dev)
     _check(call(_ptr(ws), _c.byref(nb)), "moe_align")
+    return out
+
+
+def rms_norm(x: torch.Tensor, weight: torch.Tensor, out: Optional[torch.Tensor] = None,
+             weight_bias: float = 0.0, eps: float = 1e-6, stream=None):
+    """Row RMSNorm of x [T, d] with gain weight [d] into out (a new tensor, or
+    x itself for in place).  Returns out."""
+    T, d = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    for t in (x, weight, out):
+        if t.dtype != x.dtype or not t.is_contiguous():
+            raise ValueError("x, weight and out: one dtype, contiguous")
+    _check(load().moe_rms_norm(_ptr(x), _ptr(weight), _ptr(out), T, d, act_code(x.dtype),
+                               float(weight_bias), float(eps), _stream(stream)), "moe_rms_norm")
     return out
 
 

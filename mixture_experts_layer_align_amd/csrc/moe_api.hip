@@ -307,6 +307,25 @@ int moe_qk_norm(void* q, void* k, const void* q_weight, const void* k_weight, in
   return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
+int moe_rms_norm(const void* x, const void* weight, void* out, int T, int d, int dtype,
+                 float weight_bias, float eps, void* stream) {
+  if (T < 0 || d <= 0) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const int64_t row_bytes = (int64_t)d * (dtype == MOE_BF16 ? 2 : 4);
+  if (row_bytes % 16 != 0 || row_bytes > RMS_MAX_ROW_BYTES) return MOE_ERR_UNSUPPORTED;
+  if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(weight_bias)) return MOE_ERR_INVALID;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || weight == nullptr || out == nullptr) return MOE_ERR_INVALID;
+  // out is x itself or does not overlap it
+  const char* xb = static_cast<const char*>(x);
+  const char* ob = static_cast<const char*>(out);
+  const int64_t bytes = row_bytes * T;
+  if (ob != xb && ob < xb + bytes && xb < ob + bytes) return MOE_ERR_INVALID;
+  const hipError_t e = launch_rms_norm(dtype == MOE_BF16 ? ACT_BF16 : ACT_F32, x, weight, out, T,
+                                       d, weight_bias, eps, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
 int moe_route(const void* x, const void* w_router, const float* logit_bias, int T, int d, int E,
               int k, int act_dtype, float* logits, int32_t* topk_ids, float* topk_w,
               void* workspace, size_t* workspace_bytes, void* stream) {

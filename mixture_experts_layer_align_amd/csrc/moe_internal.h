@@ -172,13 +172,17 @@ hipError_t launch_combine(int act_dtype, const float* y, int nsplit, int64_t spl
                           const int32_t* inv_pos, const float* w, int T, int k, int d, void* out,
                           hipStream_t st);
 
-// ------------------------------------------------------------ QK-norm
+// ------------------------------------------------------------ RMS norms
 
 // In-place per-head RMS normalisation of q [T, nq, head_dim] and k [T, nk,
-// head_dim] (weights [head_dim] each, all in the activation dtype);
-// head_dim * element size must be 128, 256 or 512 (bf16: 64/128/256 elements).
+// head_dim] (weights [head_dim] each, all in the activation dtype).
 hipError_t launch_qk_norm(int act_dtype, void* q, void* k, const void* wq, const void* wk, int T,
                           int nq, int nk, int head_dim, float weight_bias, float eps,
                           hipStream_t st);
+// Row RMSNorm of x [T, d] into y [T, d] (y may be x), gain [d].  d * element
+// size must be a multiple of 16 bytes and at most RMS_MAX_ROW_BYTES.
+constexpr int RMS_MAX_ROW_BYTES = 32768;
+hipError_t launch_rms_norm(int act_dtype, const void* x, const void* w, void* y, int T, int d,
+                           float weight_bias, float eps, hipStream_t st);
 
 }  // namespace moe

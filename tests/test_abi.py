@@ -210,3 +210,24 @@ def test_noalloc_scratch_size_matches_header():
     src = open(os.path.join(ROOT, "include", "libmoe.h")).read()
     m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
     assert m and int(m.group(1)) << int(m.group(2)) == B.MOE_NOALLOC_SCRATCH_BYTES
+
+
+def test_rms_norm_validation_on_host():
+    lib = B.load()
+    vp = ctypes.c_void_p
+    # row bytes not a multiple of 16, or above 32 KiB: unsupported
+    assert lib.moe_rms_norm(vp(256), vp(256), vp(1 << 20), 4, 100, B.MOE_BF16, 0.0, 1e-6,
+                            None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_rms_norm(vp(256), vp(256), vp(1 << 30), 4, 16392, B.MOE_BF16, 0.0, 1e-6,
+                            None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_rms_norm(vp(256), vp(256), vp(1 << 30), 4, 8196, B.MOE_F32, 0.0, 1e-6,
+                            None) == B.MOE_ERR_UNSUPPORTED
+    # negative eps, missing pointers, partial overlap of out and x
+    assert lib.moe_rms_norm(vp(256), vp(256), vp(1 << 20), 4, 2048, B.MOE_BF16, 0.0, -1.0,
+                            None) == B.MOE_ERR_INVALID
+    assert lib.moe_rms_norm(None, vp(256), vp(1 << 20), 4, 2048, B.MOE_BF16, 0.0, 1e-6,
+                            None) == B.MOE_ERR_INVALID
+    assert lib.moe_rms_norm(vp(4096), vp(256), vp(4096 + 4096), 4, 2048, B.MOE_BF16, 0.0, 1e-6,
+                            None) == B.MOE_ERR_INVALID
+    # an empty batch is valid and launches nothing
+    assert lib.moe_rms_norm(None, None, None, 0, 2048, B.MOE_BF16, 0.0, 1e-6, None) == B.MOE_OK
