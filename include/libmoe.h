@@ -167,13 +167,13 @@ int moe_align(const int32_t* topk_ids, int T, int E, int k, int block_m,
  * concatenated into one [d, 2*d_ff] matrix, gate columns first ("La fusion de
  * noyaux", section 4.2); SiLU(g)*u is applied to the fp32 accumulators before
  * the single store of h.  The top-k weights are applied in the combine.
- * Intermediates: the per-slot expert outputs y in fp32; h in fp32 for fp32
- * activations, and for bf16 activations with more significant bits than
- * bf16 holds: as a pair of bf16 (h's high and low halves, 16 significant
- * bits) for thin blocks (the weight-streaming GEMMs of decode batches), in
- * fp16 (11 significant bits; |h| must stay below 65504, beyond which the
- * output shows infinities) for thick blocks (the MFMA-tiled GEMMs of prefill
- * batches).  With one bf16 rounding of h, rows of d = 4096 and 7168 layers
+ * Intermediates: fp32 throughout for fp32 activations.  For bf16
+ * activations h keeps more significant bits than bf16 holds: a pair of bf16
+ * (h's high and low halves, 16 significant bits) for thin blocks (the
+ * weight-streaming GEMMs of decode batches), with the per-slot expert outputs
+ * y in fp32; fp16 (11 significant bits) for thick blocks (the MFMA-tiled
+ * GEMMs of prefill batches), where y is fp16 too.  On that path |h| and |y|
+ * must stay below 65504, beyond which the output shows infinities.  With one bf16 rounding of h, rows of d = 4096 and 7168 layers
  * measured up to 2.2e-2 * RMS off the exact result against a 2e-2 bound,
  * where the output's own rounding alone stays at 1.74e-2.
  * ------------------------------------------------------------------------- */

@@ -13,13 +13,53 @@
 // workgroup walks the k-splits one memory round trip after another.  There a
 // one-wave workgroup covers 256 elements (4 per lane) and every row load of
 // NS splits x JB slots is issued before the first add.
+//
+// YH: the expert rows are fp16 (the MFMA-tiled down GEMM's outputs) rather
+// than fp32; they are widened exactly and summed the same way.
 #include "moe_common.h"
 #include "moe_internal.h"
 
 namespace moe {
 
-template <int ACT, int JB>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, int nsplit,
+namespace {
+
+// N consecutive values of expert row `row` (element offset c) as fp32
+template <bool YH, int N>
+__device__ __forceinline__ void load_row(const void* base, int64_t elem, float* v) {
+  if constexpr (YH) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const char* p = reinterpret_cast<const char*>(base) + elem * 2;
+    uint32_t w[N / 2];
+    if constexpr (N == 8) {
+      const u32x4 r = ld16(p);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = r[q];
+    } else {
+      const u32x2 r = ld8(p);
+      w[0] = r[0];
+      w[1] = r[1];
+    }
+#pragma unroll
+    for (int q = 0; q < N / 2; ++q) {
+      const f16x2 h = __builtin_bit_cast(f16x2, w[q]);
+      v[2 * q] = (float)h[0];
+      v[2 * q + 1] = (float)h[1];
+    }
+  } else {
+    const float* p = reinterpret_cast<const float*>(base) + elem;
+#pragma unroll
+    for (int h = 0; h < N / 4; ++h) {
+      const u32x4 r = ld16(p + 4 * h);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[4 * h + q] = __uint_as_float(r[q]);
+    }
+  }
+}
+
+}  // namespace
+
+template <int ACT, int JB, bool YH>
+__global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, int nsplit,
                                                  int64_t split_stride,
                                                  const int32_t* __restrict__ inv_pos,
                                                  const float* __restrict__ w, int k, int d,
@@ -53,13 +93,10 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, in
       for (int s = 0; s < nsplit; ++s) {
 #pragma unroll
         for (int jj = 0; jj < JB; ++jj) {
-          const float* row = y + (int64_t)pos[jj] * d + c0 + s * split_stride;
+          float r[VEC];
+          load_row<YH, VEC>(y, (int64_t)pos[jj] * d + c0 + s * split_stride, r);
 #pragma unroll
-          for (int h = 0; h < VEC / 4; ++h) {
-            const u32x4 r = ld16(row + 4 * h);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) ys[jj][4 * h + q] += __uint_as_float(r[q]);
-          }
+          for (int v = 0; v < VEC; ++v) ys[jj][v] += r[v];
         }
       }
 #pragma unroll
@@ -82,8 +119,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, in
   }
 }
 
-template <int ACT, int JB, int NS>
-__global__ __launch_bounds__(64) void k_combine_narrow(const float* __restrict__ y, int nsplit,
+template <int ACT, int JB, int NS, bool YH>
+__global__ __launch_bounds__(64) void k_combine_narrow(const void* __restrict__ y, int nsplit,
                                                        int64_t split_stride,
                                                        const int32_t* __restrict__ inv_pos,
                                                        const float* __restrict__ w, int k, int d,
@@ -111,12 +148,13 @@ __global__ __launch_bounds__(64) void k_combine_narrow(const float* __restrict__
     for (int s0 = 0; s0 < nsplit; s0 += NS) {
       // NS splits per pass; a split past the last reloads the last and is
       // not added (splits are still added in order)
-      u32x4 r[NS][JB];
+      float r[NS][JB][4];
 #pragma unroll
       for (int q = 0; q < NS; ++q) {
         const int64_t so = (int64_t)min(s0 + q, nsplit - 1) * split_stride;
 #pragma unroll
-        for (int jj = 0; jj < JB; ++jj) r[q][jj] = ld16(y + so + (int64_t)pos[jj] * d + c0);
+        for (int jj = 0; jj < JB; ++jj)
+          load_row<YH, 4>(y, so + (int64_t)pos[jj] * d + c0, r[q][jj]);
       }
 #pragma unroll
       for (int q = 0; q < NS; ++q)
@@ -124,7 +162,7 @@ __global__ __launch_bounds__(64) void k_combine_narrow(const float* __restrict__
 #pragma unroll
           for (int jj = 0; jj < JB; ++jj)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) ys[jj][v] += __uint_as_float(r[q][jj][v]);
+            for (int v = 0; v < 4; ++v) ys[jj][v] += r[q][jj][v];
         }
     }
 #pragma unroll
@@ -147,31 +185,33 @@ __global__ __launch_bounds__(64) void k_combine_narrow(const float* __restrict__
 // Token x 2048-element chunks below which the one-wave variant is used.
 constexpr int NARROW_BELOW = 256;
 
-template <int ACT, int JB>
-static void launch_narrow(const float* y, int nsplit, int64_t split_stride, const int32_t* inv_pos,
+template <int ACT, int JB, bool YH>
+static void launch_narrow(const void* y, int nsplit, int64_t split_stride, const int32_t* inv_pos,
                           const float* w, int T, int k, int d, void* out, hipStream_t st) {
   const dim3 grid((unsigned)T, (unsigned)((d + 255) / 256));
   char* o = reinterpret_cast<char*>(out);
   if (nsplit >= 4)
-    hipLaunchKernelGGL((k_combine_narrow<ACT, JB, 4>), grid, dim3(64), 0, st, y, nsplit,
+    hipLaunchKernelGGL((k_combine_narrow<ACT, JB, 4, YH>), grid, dim3(64), 0, st, y, nsplit,
                        split_stride, inv_pos, w, k, d, o);
   else if (nsplit >= 2)
-    hipLaunchKernelGGL((k_combine_narrow<ACT, JB, 2>), grid, dim3(64), 0, st, y, nsplit,
+    hipLaunchKernelGGL((k_combine_narrow<ACT, JB, 2, YH>), grid, dim3(64), 0, st, y, nsplit,
                        split_stride, inv_pos, w, k, d, o);
   else
-    hipLaunchKernelGGL((k_combine_narrow<ACT, JB, 1>), grid, dim3(64), 0, st, y, nsplit,
+    hipLaunchKernelGGL((k_combine_narrow<ACT, JB, 1, YH>), grid, dim3(64), 0, st, y, nsplit,
                        split_stride, inv_pos, w, k, d, o);
 }
 
-hipError_t launch_combine(int act, const float* y, int nsplit, int64_t split_stride,
-                          const int32_t* inv_pos, const float* w, int T, int k, int d, void* out,
-                          hipStream_t st) {
+template <bool YH>
+static hipError_t launch_combine_y(int act, const void* y, int nsplit, int64_t split_stride,
+                                   const int32_t* inv_pos, const float* w, int T, int k, int d,
+                                   void* out, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const int vec = act == ACT_BF16 ? 8 : 4;
   const dim3 grid((unsigned)T, (unsigned)((d + 256 * vec - 1) / (256 * vec)));
   const int jb = k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : 8;
   if ((int64_t)T * ((d + 2047) / 2048) < NARROW_BELOW) {
-#define MOE_NARROW(A_, JB_) launch_narrow<A_, JB_>(y, nsplit, split_stride, inv_pos, w, T, k, d, out, st)
+#define MOE_NARROW(A_, JB_) \
+  launch_narrow<A_, JB_, YH>(y, nsplit, split_stride, inv_pos, w, T, k, d, out, st)
     if (act == ACT_BF16) {
       if (jb == 1) MOE_NARROW(ACT_BF16, 1);
       else if (jb == 2) MOE_NARROW(ACT_BF16, 2);
@@ -190,7 +230,7 @@ hipError_t launch_combine(int act, const float* y, int nsplit, int64_t split_str
   // requests outstanding and 3-5 % slower at 8192-16384 tokens, top-8)
   const int jbw = jb > 4 ? 4 : jb;
 #define MOE_COMBINE(A_, JB_)                                                                  \
-  hipLaunchKernelGGL((k_combine<A_, JB_>), grid, dim3(256), 0, st, y, nsplit, split_stride, \
+  hipLaunchKernelGGL((k_combine<A_, JB_, YH>), grid, dim3(256), 0, st, y, nsplit, split_stride, \
                      inv_pos, w, k, d, reinterpret_cast<char*>(out))
   if (act == ACT_BF16) {
     if (jbw == 1) MOE_COMBINE(ACT_BF16, 1);
@@ -203,6 +243,14 @@ hipError_t launch_combine(int act, const float* y, int nsplit, int64_t split_str
   }
 #undef MOE_COMBINE
   return hipGetLastError();
+}
+
+hipError_t launch_combine(int act, const void* y, bool y_f16, int nsplit, int64_t split_stride,
+                          const int32_t* inv_pos, const float* w, int T, int k, int d, void* out,
+                          hipStream_t st) {
+  return y_f16 ? launch_combine_y<true>(act, y, nsplit, split_stride, inv_pos, w, T, k, d, out, st)
+               : launch_combine_y<false>(act, y, nsplit, split_stride, inv_pos, w, T, k, d, out,
+                                         st);
 }
 
 }  // namespace moe

@@ -314,9 +314,11 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
   using C = Cfg<WT, HALF>;
   constexpr int S = C::STAGES;
   static_assert(TILED_MIN_KCHUNK / TBK >= S + 2, "the pipeline needs nk > S (nk even)");
-  // gate|up's MFMAs compute the transposed blocks (weights as the first
-  // operand; the two operands' lane layouts are the same) for its epilogue
-  constexpr bool TRANSPOSED = EPI == EPI_SILU_MUL;
+  // the MFMAs compute the transposed blocks (weights as the first operand;
+  // the two operands' lane layouts are the same), so a lane ends with 4
+  // consecutive output columns of one row: one 8-byte store of 4 fp16 h
+  // (gate|up) or y (down) values
+  constexpr bool TRANSPOSED = true;
   // the down GEMM runs on fp16 operands: h as the gate|up epilogue stored it
   // (fp16, 11 significant bits) and the weights converted exactly
   constexpr bool F16 = EPI == EPI_STORE;
@@ -562,7 +564,7 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
     for (int ni = 0; ni < 8; ++ni) asm volatile("" : "+a"(acc[mi][ni]));
 
   // ---------------------------------------------------- epilogue
-  if constexpr (TRANSPOSED) {
+  if constexpr (EPI == EPI_SILU_MUL) {
     // gate|up: the MFMAs took the weight fragment as their first operand, so
     // each 16 x 16 block came out transposed: acc[mi][ni] lane (lm, lg) holds
     // token row wm*128 + mi*16 + lm and the 4 consecutive weight columns
@@ -607,35 +609,40 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
       }
     }
   } else {
-    // down: acc[mi][ni] lane (lm, lg) holds rows 4lg + r of the 16 x 16
-    // block (mi, ni) and column ntw*256 + wn*128 + 16ni + lm (the output is
-    // fp32 and its stores are bound by HBM bandwidth, which the transposed
-    // layout's wider stores do not change: measured 1-5 % slower)
-    float sc[8];  // fp8: per-column scales of the lane's 8 columns
+    // down: acc[mi][ni] lane (lm, lg) holds token row wm*128 + mi*16 + lm and
+    // the 4 consecutive output columns ntw*256 + wn*128 + 16ni + 4lg + r,
+    // scaled (fp8) and stored as fp16 (its 11 significant bits keep the
+    // combine's sum within the output's own rounding; half the bytes of fp32)
+    const int lrow0 = wm * 128 + lm;
+    const int c0 = ntw * TBN + wn * 128 + 4 * lg;
+    f32x4 sc[8];  // fp8: scales of the lane's 4 columns of each block
     if constexpr (WT == W_FP8) {
-      const float* sb = p.scale + (int64_t)e * p.scale_estride;
+      const float* sb = p.scale + (int64_t)e * p.scale_estride + c0;
 #pragma unroll
-      for (int ni = 0; ni < 8; ++ni) sc[ni] = sb[ntw * TBN + wn * 128 + 16 * ni + lm];
-    }
-    // the lane's row wm*128 + 4*lg + (mi*16 + r) holds a routed slot iff
-    // mi*16 + r < vrows (a compile-time offset against one register)
-    const int vrows = n_valid - (wm * 128 + 4 * lg);
+      for (int ni = 0; ni < 8; ++ni) {
+        const u32x4 v = ld16(sb + 16 * ni);
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (mi * 16 + r >= vrows) continue;  // padding slot
-        const int lrow = wm * 128 + mi * 16 + 4 * lg + r;
-        const int64_t prow = p0 + lrow;
-        float* dst = reinterpret_cast<float*>(p.out) + ks * p.out_split_stride + prow * p.out_ld +
-                     ntw * TBN + wn * 128 + lm;
-#pragma unroll
-        for (int ni = 0; ni < 8; ++ni) {
-          float v = acc[mi][ni][r];
-          if constexpr (WT == W_FP8) v *= sc[ni];
-          dst[ni * 16] = v;
-        }
+        for (int r = 0; r < 4; ++r) sc[ni][r] = __uint_as_float(v[r]);
       }
+    }
+    const int vrows = n_valid - lrow0;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      if (mi * 16 >= vrows) continue;  // padding slot
+      uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + ks * p.out_split_stride +
+                      (int64_t)(p0 + lrow0 + mi * 16) * p.out_ld + c0;
+#pragma unroll
+      for (int ni = 0; ni < 8; ++ni) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = acc[mi][ni][r];
+          if constexpr (WT == W_FP8) v[r] *= sc[ni][r];
+        }
+        const u32x2 o = {pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(dst + ni * 16) = o;
+      }
+    }
   }
   return claimed;
 }

@@ -481,8 +481,12 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   const bool h_pair = !tiled && act == ACT_BF16;
   char* h = c.take<char>(std::max<int64_t>(cap * dff * ab, 1));
   char* h_lo = h_pair ? c.take<char>(std::max<int64_t>(cap * dff * 2, 1)) : nullptr;
-  // per-slot expert outputs (fp32), or their k-split partial sums
-  float* y = c.take<float>(std::max<int64_t>(dn_split * cap * d, 1));
+  // per-slot expert outputs, or their k-split partial sums: fp32 from the
+  // weight-streaming GEMM, fp16 from the MFMA-tiled one (the tiled GEMM's
+  // fp32 stores were bound by HBM write bandwidth; fp16's 11 bits keep the
+  // output within its own rounding, like h's)
+  const bool y_f16 = tiled;
+  void* y = c.take<char>(std::max<int64_t>(dn_split * cap * d * (y_f16 ? 2 : 4), 1));
   float* gu_part = gu_split > 1 ? c.take<float>(gu_split * cap * 2 * dff) : nullptr;
   bool query;
   rc = check_ws(workspace, workspace_bytes, c.off, &query);
@@ -607,7 +611,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g2.ksplit = dn_split;
   g2.kchunk = dn_chunk;
   g2.wgs = dn_wgs;
-  g2.partial = y;
+  g2.partial = static_cast<float*>(y);
   g2.partial_ld = d;
   g2.partial_split_stride = cap * d;
   g2.out_split_stride = cap * d;
@@ -619,7 +623,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   if (e != hipSuccess) return MOE_ERR_DEVICE;
 
   trace_mark(tr, &kidx, "combine", st);
-  e = launch_combine(act, y, dn_split, cap * d, inv, tw, T, k, d, out, st);
+  e = launch_combine(act, y, y_f16, dn_split, cap * d, inv, tw, T, k, d, out, st);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   trace_mark(tr, &kidx, nullptr, st);
   if (tr != nullptr) tr->n_kernels = kidx - 1;

@@ -166,11 +166,11 @@ hipError_t launch_route_align_small(const float* partial, int nsplit, int64_t sp
 
 // ------------------------------------------------------------ combine
 
-// y: per-slot expert outputs, fp32 [nsplit][cap, d] (k-split partial sums,
-// added in split order before the weighting)
-hipError_t launch_combine(int act_dtype, const float* y, int nsplit, int64_t split_stride,
-                          const int32_t* inv_pos, const float* w, int T, int k, int d, void* out,
-                          hipStream_t st);
+// y: per-slot expert outputs [nsplit][cap, d] (k-split partial sums, added in
+// split order before the weighting), fp32 or, with y_f16, fp16
+hipError_t launch_combine(int act_dtype, const void* y, bool y_f16, int nsplit,
+                          int64_t split_stride, const int32_t* inv_pos, const float* w, int T,
+                          int k, int d, void* out, hipStream_t st);
 
 // ------------------------------------------------------------ RMS norms
 
