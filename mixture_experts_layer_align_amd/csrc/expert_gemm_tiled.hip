@@ -307,7 +307,9 @@ constexpr int slot_of(int i, int n, int span) { return (i * span) / n; }
 // barrier that frees the LDS ring.  Thread 0 claims the workgroup's next tile
 // from *next as the tile starts and returns the counter's old value; other
 // threads return 0.
-template <int EPI, int WT, bool HALF>
+// MIL: the wave's 16-row fragments that hold routed slots (the rest are
+// padding, their MFMAs and fragment reads left out); MI for every full tile.
+template <int EPI, int WT, bool HALF, int MIL>
 __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint32_t lds_base,
                                         int p0, int e, int n_valid, int nt, int ks,
                                         int* next) {
@@ -434,7 +436,7 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
   auto read = [&](auto r_c, Frags<WT>& f, uint32_t st_off) __attribute__((always_inline)) {
     constexpr int r = decltype(r_c)::value;
     if constexpr (r < MI) {
-      f.a[r] = lds_read_b128<r * 1024>(st_off + a_base);
+      if constexpr (r < MIL) f.a[r] = lds_read_b128<r * 1024>(st_off + a_base);
     } else if constexpr (WT == W_FP8) {
       f.b.b8[r - MI] = lds_read_tr8(st_off + b_base[r - MI]);
     } else {
@@ -468,7 +470,9 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
         bf = wcur[ni];
       else
         bf = u32x4{cur.b.lo[ni][0], cur.b.lo[ni][1], cur.b.hi[ni][0], cur.b.hi[ni][1]};
-      if constexpr (FIRST)
+      if constexpr (mi >= MIL)
+        ;  // a padding fragment
+      else if constexpr (FIRST)
         if constexpr (TRANSPOSED)
           mfma_zero<F16>(acc[mi][ni], bf, cur.a[mi]);
         else
@@ -722,8 +726,12 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
     const int ev = p.tile_rows[2 * row + 1];
     const int e = ev & 0xFFFF, n_valid = ev >> 16;
     const int claimed =
-        full ? run_tile<EPI, WT, false>(p, lds, lds_base, p0, e, n_valid, nt, ks, next)
-             : run_tile<EPI, WT, true>(p, lds, lds_base, p0, e, n_valid, 2 * nt, ks, next);
+        full ? run_tile<EPI, WT, false, MI>(p, lds, lds_base, p0, e, n_valid, nt, ks, next)
+        // a half row with at most 32 routed slots (light experts' last
+        // rows): two live fragments per wave
+        : n_valid <= 32
+            ? run_tile<EPI, WT, true, 2>(p, lds, lds_base, p0, e, n_valid, 2 * nt, ks, next)
+            : run_tile<EPI, WT, true, MI>(p, lds, lds_base, p0, e, n_valid, 2 * nt, ks, next);
     // every wave is done with the tile's LDS stages
     __syncthreads();
     id = w_begin + publish(claimed);
