@@ -727,10 +727,12 @@ __global__ __launch_bounds__(256) void k_expert_tiled(const StreamGemmArgs p) {
     const int e = ev & 0xFFFF, n_valid = ev >> 16;
     const int claimed =
         full ? run_tile<EPI, WT, false, MI>(p, lds, lds_base, p0, e, n_valid, nt, ks, next)
-        // a half row with at most 32 routed slots (light experts' last
-        // rows): two live fragments per wave
+        // a half row with at most 32 or 64 routed slots (light experts'
+        // last rows): two or four live fragments per wave
         : n_valid <= 32
             ? run_tile<EPI, WT, true, 2>(p, lds, lds_base, p0, e, n_valid, 2 * nt, ks, next)
+        : n_valid <= 64
+            ? run_tile<EPI, WT, true, 4>(p, lds, lds_base, p0, e, n_valid, 2 * nt, ks, next)
             : run_tile<EPI, WT, true, MI>(p, lds, lds_base, p0, e, n_valid, 2 * nt, ks, next);
     // every wave is done with the tile's LDS stages
     __syncthreads();
