@@ -9,15 +9,18 @@
 // section: heads of 64-256 values, and the weight bias some models add).
 //
 // gfx950 mapping, one shape for both: a row of R 16-byte pieces belongs to a
-// group of L lanes of one wave (L = R for a power-of-two R below 64, else
-// L = 64), each lane holding C = ceil(R / L) pieces: pieces p, p + L, p + 2L,
+// group of L lanes (L = R for a power-of-two R below 64; 64 lanes, one wave,
+// for rows of up to 255 pieces; 256 lanes, the whole workgroup, for longer
+// rows), each lane holding C = ceil(R / L) pieces: pieces p, p + L, p + 2L,
 // ..., so every load of the group is one contiguous run.  The lane sums the
-// squares of its pieces in fp32; an xor butterfly over the L lanes (offsets
-// below L never leave the group) gives every lane the row's sum; then the
-// scale and the gain, and one 16-byte store per piece.  No LDS, no barrier: a
-// wave handles 64 / L rows at once, independently.  x is read and y written
-// exactly once, with non-temporal loads and stores, so the kernel streams at
-// HBM speed.
+// squares of its pieces in fp32; an xor butterfly over the wave's lanes of
+// the row (offsets below L never leave the group) and, for a row of four
+// waves, their four partial sums added in wave order through LDS give every
+// lane the row's sum; then the scale and the gain, and one 16-byte store per
+// piece.  Spreading a long row over the workgroup keeps each lane at a few
+// pieces: a copy of the same bytes measured 6.2-6.4 TB/s with one piece in
+// flight per lane and 4.7-5.6 TB/s with fourteen.  x is read and y written
+// exactly once, with non-temporal loads and stores.
 //
 // A launch covers up to two row sets (segments), each a contiguous array of
 // rows with its own gain: the q heads and the k heads of QK-norm are two
@@ -68,20 +71,20 @@ __device__ __forceinline__ u32x4 pack(const float* f) {
 
 }  // namespace
 
-// L lanes per row, up to C pieces per lane; MASK: pieces past R exist in the
-// lane layout (R not a multiple of L) and are skipped.
+// L lanes per row (1..64, or 256), up to C pieces per lane; MASK: pieces
+// past R exist in the lane layout (R not a multiple of L) and are skipped.
 template <int ACT, int L, int C, bool MASK>
 __global__ __launch_bounds__(256) void k_rms_rows(RowSet s0, RowSet s1, int n, int R,
                                                   float weight_bias, float eps) {
   constexpr int V = ACT == ACT_BF16 ? 8 : 4;  // values per 16-byte piece
-  constexpr int ROWS_PER_WAVE = WAVE / L;
+  constexpr int ROWS_PER_WG = 256 / L;
+  constexpr int WAVES_PER_ROW = L > WAVE ? L / WAVE : 1;
+  static_assert(L <= WAVE || L == 256, "a row is a lane group or the whole workgroup");
   const bool second = (int64_t)blockIdx.x >= s0.blocks;  // uniform per workgroup
   const RowSet s = second ? s1 : s0;
   const int64_t blk = second ? (int64_t)blockIdx.x - s0.blocks : (int64_t)blockIdx.x;
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int64_t wave = blk * (blockDim.x / WAVE) + (threadIdx.x / WAVE);
-  const int64_t row = wave * ROWS_PER_WAVE + lane / L;
-  const int p0 = lane % L;
+  const int64_t row = blk * ROWS_PER_WG + threadIdx.x / L;
+  const int p0 = threadIdx.x % L;
   const bool live = row < s.rows;
   const int64_t row_bytes = (int64_t)R * 16;
   const char* xr = s.x + (live ? row : 0) * row_bytes;
@@ -104,7 +107,16 @@ __global__ __launch_bounds__(256) void k_rms_rows(RowSet s0, RowSet s1, int n, i
     for (int v = 0; v < V; ++v) ss += f[v] * f[v];
   }
 #pragma unroll
-  for (int off = L / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  for (int off = (L < WAVE ? L : WAVE) / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if constexpr (WAVES_PER_ROW > 1) {
+    // one row per workgroup: the waves' sums, added in wave order
+    __shared__ float wave_sum[256 / WAVE];
+    if ((threadIdx.x & (WAVE - 1)) == 0) wave_sum[threadIdx.x / WAVE] = ss;
+    __syncthreads();
+    ss = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES_PER_ROW; ++w) ss += wave_sum[w];
+  }
   const float scale = rsqrtf(ss / (float)n + eps);
   if (!live) return;
 #pragma unroll
@@ -151,20 +163,24 @@ hipError_t launch_rows_any(RowSet a, RowSet b, int n, int R, float wb, float eps
       default: return launch_rows<ACT, 32, 1, false>(a, b, n, R, wb, eps, st);
     }
   }
-  const int c = (R + WAVE - 1) / WAVE;
-  const bool exact = R % WAVE == 0;
-#define MOE_ROWS(C_)                                                                   \
-  if (c <= C_)                                                                         \
-    return (exact && c == C_) ? launch_rows<ACT, WAVE, C_, false>(a, b, n, R, wb, eps, st) \
-                              : launch_rows<ACT, WAVE, C_, true>(a, b, n, R, wb, eps, st);
-  MOE_ROWS(1)
-  MOE_ROWS(2)
-  MOE_ROWS(4)
-  MOE_ROWS(8)
-  MOE_ROWS(12)
-  MOE_ROWS(16)
-  MOE_ROWS(24)
-  MOE_ROWS(32)
+  // rows of up to 255 pieces: one wave each; longer rows: the workgroup
+  if (R < 256) {
+    const int c = (R + WAVE - 1) / WAVE;
+    const bool exact = R % WAVE == 0;
+#define MOE_ROWS(L_, C_)                                                                      \
+  if (c <= C_)                                                                                \
+    return (exact && c == C_) ? launch_rows<ACT, L_, C_, false>(a, b, n, R, wb, eps, st)      \
+                              : launch_rows<ACT, L_, C_, true>(a, b, n, R, wb, eps, st);
+    MOE_ROWS(WAVE, 1)
+    MOE_ROWS(WAVE, 2)
+    MOE_ROWS(WAVE, 4)
+  }
+  const int c = (R + 255) / 256;
+  const bool exact = R % 256 == 0;
+  MOE_ROWS(256, 1)
+  MOE_ROWS(256, 2)
+  MOE_ROWS(256, 4)
+  MOE_ROWS(256, 8)
 #undef MOE_ROWS
   return hipErrorInvalidValue;
 }
