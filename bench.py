@@ -43,7 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of HIP graphs that capture one forward each")
-    ap.add_argument("--no-qk", action="store_true", help="skip the QK-norm measurement")
+    ap.add_argument("--no-qk", action="store_true", help="skip the QK-norm and RMSNorm measurements")
+    ap.add_argument("--norms", action="store_true",
+                    help="only the QK-norm and RMSNorm measurements (one JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="also run a plain device copy of MB megabytes (counter calibration)")
     return ap.parse_args()
@@ -64,7 +66,7 @@ def guarded_forwards(B, roof, layer, bias, sh, x, T):
     f0 = B.Forward(layer.w_router, bias, layer.w_gate_up, layer.w_down, sh.k,
                    layer.scale_gate_up, layer.scale_down)
     rb = f0.routing_buffers(T)
-    f0(x, routing=rb)
+    _, bm, _ = f0(x, routing=rb)
     torch.cuda.synchronize()
     active = int((rb["counts"].cpu().numpy() > 0).sum())
     work = roof.layer_work(T, sh.d, sh.d_ff, sh.E, sh.k, sh.act, sh.wdt, active)
@@ -75,7 +77,7 @@ def guarded_forwards(B, roof, layer, bias, sh, x, T):
         fwds.append(B.Forward(c(layer.w_router), bias, c(layer.w_gate_up), c(layer.w_down), sh.k,
                               c(layer.scale_gate_up), c(layer.scale_down)))
     torch.cuda.synchronize()
-    return fwds, rb, active, work
+    return fwds, rb, active, work, bm
 
 
 def timed(fwds, x, steps, warmup, graph=False):
@@ -118,7 +120,7 @@ def kernel_times(B, fwds, x, reps):
     import numpy as np
     import torch
     out = torch.empty_like(x)
-    _, bm, names = fwds[0](x, out, events=[])
+    _, _, names = fwds[0](x, out, events=[])
     torch.cuda.synchronize()
     nk = len(names)
     ev = B.HipEvents(nk + 1)
@@ -128,7 +130,7 @@ def kernel_times(B, fwds, x, reps):
         torch.cuda.synchronize()
         per += [ev.elapsed_ms(j, j + 1) for j in range(nk)]
     per /= reps
-    return {n: float(v) for n, v in zip(names, per)}, bm
+    return {n: float(v) for n, v in zip(names, per)}
 
 
 def measure(B, R, sh, layer, T, steps, warmup, graph=False):
@@ -139,9 +141,9 @@ def measure(B, R, sh, layer, T, steps, warmup, graph=False):
     dev = layer.device
     bias = make_bias(sh, sh.zipf_for(T), dev)
     x = make_tokens(sh, T, dev)
-    fwds, rb, active, work = guarded_forwards(B, R, layer, bias, sh, x, T)
+    fwds, rb, active, work, bm = guarded_forwards(B, R, layer, bias, sh, x, T)
     ms, _ = timed(fwds, x, steps, warmup, graph)
-    kern, bm = kernel_times(B, fwds, x, max(steps, 10))
+    kern = kernel_times(B, fwds, x, max(steps, 10))
     # the layer's bound: flops per byte of expert weights against the ridge
     w_bytes = work.bytes_total - 2 * T * sh.d * R.ELEM_BYTES[sh.act]
     mfma = work.flops_total / max(w_bytes, 1) > RIDGE
@@ -196,6 +198,12 @@ def main():
     from mixture_experts_layer_align_amd import _binding as B
     from mixture_experts_layer_align_amd import roofline as R
     from workloads import LAYERS, make_layer
+
+    if args.norms:
+        dev = torch.device("cuda:0")
+        print(json.dumps({"qk_norm": qk_norm_bench(B, R, dev, args.steps),
+                          "rms_norm": rms_norm_bench(B, R, dev, args.steps)}), flush=True)
+        return
 
     hc = args.config
     hsh = LAYERS[hc]
