@@ -36,7 +36,11 @@
 //     fp32 partial sums and the next kernel adds them in split order (fixed
 //     order, no atomics, no device-scope fences: on gfx950 a device-scope
 //     fence writes back and invalidates the XCD's L2, which hundreds of
-//     workgroups streaming through that L2 cannot afford);
+//     workgroups streaming through that L2 cannot afford).  For a split
+//     gate|up that next kernel is the down GEMM itself: each of its items
+//     first adds the partials of its rows and k-range and applies SiLU*up
+//     (one launch fewer; the prologue lengthens the down kernel by 3-5 µs,
+//     about what the separate reduce kernel and its launch gap took);
 //   * the epilogue runs on the fp32 accumulators before the single store:
 //     SiLU(gate) * up for the concatenated gate|up weight ("La fusion de
 //     noyaux", section 4.2, GEMM + epilogue and the SwiGLU concatenation), and
@@ -146,6 +150,68 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
 
 }  // namespace
 
+// h[p, k] = SiLU(sum_s g_s[p, k]) * sum_s u_s[p, k] for the routed rows p of
+// the block at p0 (bit r of `routed`: row p0 + r) and k in [kb, ke), splits
+// added in order, from the gate|up k-split partial sums; stored where the
+// item's main loop reads its rows (as a bf16 pair when HILO).  All 128
+// threads take part: 8 consecutive columns of one routed row per thread and
+// pass, the loads of up to FOLD_SPLITS splits in flight at once (the partials
+// come from other dies' L2 or HBM: one round trip per group of splits).  The
+// workgroups of the block's other n-tiles write the same values to the same
+// places.
+constexpr int FOLD_SPLITS = 8;
+template <int ACT, bool HILO>
+__device__ __forceinline__ void fold_split_silu(const StreamGemmArgs& p, uint32_t routed, int p0,
+                                                int kb, int ke) {
+  constexpr int ASZ = (ACT == ACT_BF16) ? 2 : 4;
+  const int K = p.K;  // gate|up's d_ff: up columns start at K
+  const int per_row = (ke - kb) / 8;
+  for (int u = threadIdx.x; u < STREAM_BM * per_row; u += 128) {
+    const int r = u / per_row;
+    if (!((routed >> r) & 1u)) continue;
+    const int c = kb + 8 * (u - r * per_row);
+    const int64_t prow = p0 + r;
+    float g[8], v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) g[j] = v[j] = 0.f;
+    const float* row = p.a_part + prow * p.a_part_ld + c;
+    for (int s0 = 0; s0 < p.a_part_nsplit; s0 += FOLD_SPLITS) {
+      u32x4 ld[FOLD_SPLITS][4];
+#pragma unroll
+      for (int i = 0; i < FOLD_SPLITS; ++i) {
+        if (s0 + i < p.a_part_nsplit) {
+          const float* src = row + (int64_t)(s0 + i) * p.a_part_stride;
+          ld[i][0] = ld16(src);
+          ld[i][1] = ld16(src + 4);
+          ld[i][2] = ld16(src + K);
+          ld[i][3] = ld16(src + K + 4);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < FOLD_SPLITS; ++i) {
+        if (s0 + i < p.a_part_nsplit) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            g[j] += __uint_as_float(ld[i][0][j]);
+            g[4 + j] += __uint_as_float(ld[i][1][j]);
+            v[j] += __uint_as_float(ld[i][2][j]);
+            v[4 + j] += __uint_as_float(ld[i][3][j]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = silu(g[j]) * v[j];
+    char* dst = const_cast<char*>(reinterpret_cast<const char*>(p.a)) + (prow * p.a_ld + c) * ASZ;
+    if constexpr (HILO)
+      store_bf16_pair<8>(dst, const_cast<char*>(reinterpret_cast<const char*>(p.a_lo)) +
+                                  (prow * p.a_ld + c) * 2,
+                         v);
+    else
+      store_act<ACT>(dst, v, 8);
+  }
+}
+
 // One item = (32-row block, n-tile, k-split) of the launch.  HILO: the token
 // rows come as bf16 pairs (p.a high halves, p.a_lo low halves) and every
 // weight fragment is applied to both, which carries h into the down GEMM at
@@ -225,6 +291,15 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
                                (int64_t)(kb / KSTEP) * p.w_ld + wcol
                          : nullptr;
   u32x4* ring = lds + slab * S * RPL * WAVE;
+  if constexpr (EPI == EPI_STORE) {
+    if (p.a_part != nullptr) {  // uniform
+      // lanes 0-15 hold rows 0-15 (q = 0) and 16-31 (q = 1)
+      const uint32_t routed = (uint32_t)(ballot(rvalid[0]) & 0xFFFFu) |
+                              ((uint32_t)(ballot(rvalid[1]) & 0xFFFFu) << 16);
+      fold_split_silu<ACT, HILO>(p, routed, p0, kb, ke);
+      __syncthreads();  // h of the item's rows and k-range is in place
+    }
+  }
 
   f32x4 acc[2][CPL];
 #pragma unroll
@@ -389,7 +464,7 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
   // -------------------------------------------------------- split-K partials
   // With several k-splits each split stores its (scaled) fp32 sums for the
   // routed rows; a later kernel adds the splits in split order (for gate|up
-  // the split-reduce kernel, which also applies SiLU*up; for down the
+  // the down GEMM, whose items first form h from them; for down the
   // combine).  The kernel boundary orders the stores before those reads, so
   // no device-scope fence or atomic is needed here.
   if (p.ksplit > 1) {
@@ -497,60 +572,6 @@ __global__ __launch_bounds__(128) void k_expert_stream(const StreamGemmArgs p) {
     __syncthreads();  // the previous item's epilogue is done with the ring
     stream_item<ACT, WT, EPI, HILO>(p, i, lds);
   }
-}
-
-// h[p, n] = SiLU(sum_s g_s[p, n]) * sum_s u_s[p, n] for the routed rows p,
-// splits added in order.  One workgroup per (row, 2048-column chunk).
-template <int ACT>
-__global__ __launch_bounds__(256) void k_splitk_silu(const float* __restrict__ part, int nsplit,
-                                                     int64_t split_stride, int64_t part_ld,
-                                                     const int32_t* __restrict__ sorted_ids,
-                                                     int d_ff, char* __restrict__ h,
-                                                     char* __restrict__ h_lo) {
-  constexpr int ASZ = ACT == ACT_BF16 ? 2 : 4;
-  const int64_t p = blockIdx.x;
-  if (sorted_ids[p] < 0) return;
-  const int n0 = (blockIdx.y * 256 + threadIdx.x) * 8;
-  if (n0 >= d_ff) return;
-  float g[8], u[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) g[j] = u[j] = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* row = part + s * split_stride + p * part_ld;
-#pragma unroll
-    for (int hlf = 0; hlf < 2; ++hlf) {
-      const u32x4 a = ld16(row + n0 + 4 * hlf);
-      const u32x4 b = ld16(row + d_ff + n0 + 4 * hlf);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        g[4 * hlf + j] += __uint_as_float(a[j]);
-        u[4 * hlf + j] += __uint_as_float(b[j]);
-      }
-    }
-  }
-  float v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = silu(g[j]) * u[j];
-  if (ACT == ACT_BF16 && h_lo != nullptr)
-    store_bf16_pair<8>(h + (p * d_ff + n0) * ASZ, h_lo + (p * d_ff + n0) * 2, v);
-  else
-    store_act<ACT>(h + (p * d_ff + n0) * ASZ, v, 8);
-}
-
-hipError_t launch_splitk_silu(int act, const float* part, int nsplit, int64_t split_stride,
-                              int64_t part_ld, const int32_t* sorted_ids, int64_t rows, int d_ff,
-                              void* h, void* h_lo, hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
-  const dim3 grid((unsigned)rows, (unsigned)((d_ff + 2047) / 2048));
-  if (act == ACT_BF16)
-    hipLaunchKernelGGL(k_splitk_silu<ACT_BF16>, grid, dim3(256), 0, st, part, nsplit, split_stride,
-                       part_ld, sorted_ids, d_ff, reinterpret_cast<char*>(h),
-                       reinterpret_cast<char*>(h_lo));
-  else
-    hipLaunchKernelGGL(k_splitk_silu<ACT_F32>, grid, dim3(256), 0, st, part, nsplit, split_stride,
-                       part_ld, sorted_ids, d_ff, reinterpret_cast<char*>(h),
-                       reinterpret_cast<char*>(h_lo));
-  return hipGetLastError();
 }
 
 int stream_tile_cols(int w_dtype, int epi) {

@@ -580,17 +580,17 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   e = tiled ? launch_tiled_gemm(EPI_SILU_MUL, wdt, bm, g, st)
             : launch_stream_gemm(act, wdt, EPI_SILU_MUL, g, st);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
-  if (gu_split > 1) {
-    trace_mark(tr, &kidx, "gate_up_reduce", st);
-    e = launch_splitk_silu(act, gu_part, gu_split, cap * 2 * dff, 2 * (int64_t)dff, sorted, cap,
-                           dff, h, h_lo, st);
-    if (e != hipSuccess) return MOE_ERR_DEVICE;
-  }
 
   StreamGemmArgs g2{};
   g2.a = h;
   g2.a_lo = h_lo;
   g2.a_ld = dff;
+  // a split gate|up leaves fp32 partials: the down GEMM's items add them and
+  // apply SiLU*up for their own rows and k-range before using them
+  g2.a_part = gu_split > 1 ? gu_part : nullptr;
+  g2.a_part_nsplit = gu_split;
+  g2.a_part_ld = 2 * (int64_t)dff;
+  g2.a_part_stride = cap * 2 * dff;
   g2.a_mode = A_PADDED;
   g2.sorted_ids = sorted;
   g2.topk = k;

@@ -34,6 +34,15 @@ struct StreamGemmArgs {
   const void* a_lo;       // bf16 rows only: the low halves of rows carried as a pair of
                           //   bf16 (value = a + a_lo, same layout), or NULL
   int64_t a_ld;           // elements
+  // EPI_STORE: the gate|up k-split partial sums [a_part_nsplit][rows][a_part_ld]
+  // (gate columns [0, K), up columns [K, 2K)), or NULL.  Given, each item first
+  // forms h = SiLU(sum of gate partials) * (sum of up partials) for its block's
+  // routed rows over its k-range, splits added in order, and writes it into a
+  // (and a_lo), where its main loop then reads its rows.
+  const float* a_part;
+  int a_part_nsplit;
+  int64_t a_part_ld;
+  int64_t a_part_stride;
   int a_mode;
   const int32_t* sorted_ids;
   int topk;
@@ -81,12 +90,6 @@ int stream_tile_cols(int w_dtype, int epi);
 // K granularity of one k-step.
 int stream_kstep(int w_dtype);
 
-// h = SiLU(sum of gate partials) * (sum of up partials), splits in order, for
-// the rows whose slot holds a routed entry.
-// h_lo (bf16 only, or NULL): also store h's low halves, as out_lo above.
-hipError_t launch_splitk_silu(int act_dtype, const float* part, int nsplit, int64_t split_stride,
-                              int64_t part_ld, const int32_t* sorted_ids, int64_t rows, int d_ff,
-                              void* h, void* h_lo, hipStream_t st);
 hipError_t launch_stream_gemm(int act_dtype, int w_dtype, int epi, const StreamGemmArgs& a,
                               hipStream_t st);
 

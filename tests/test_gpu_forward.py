@@ -71,6 +71,10 @@ SMALL = [
     (8, 2, 256, 256, "bf16", "fp8", 257, 1.2),
     (4, 2, 128, 128, "f32", "f32", 300, 0.5),
     (8, 2, 128, 128, "bf16", "bf16", 0, None),       # empty batch
+    # few rows, long K: gate|up splits K and the down GEMM forms h from the
+    # fp32 partials (fp32 h; bf16-pair h)
+    (8, 2, 512, 256, "f32", "f32", 2, None),
+    (16, 4, 1024, 256, "bf16", "bf16", 2, None),
     # >= 64 routed rows per expert and d % 256 == 0: the MFMA-tiled GEMM
     (4, 2, 256, 256, "bf16", "bf16", 300, None),
     (8, 2, 512, 384, "bf16", "bf16", 700, 1.2),      # skewed, ragged blocks
