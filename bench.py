@@ -43,9 +43,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of HIP graphs that capture one forward each")
-    ap.add_argument("--no-qk", action="store_true", help="skip the QK-norm and RMSNorm measurements")
-    ap.add_argument("--norms", action="store_true",
-                    help="only the QK-norm and RMSNorm measurements (one JSON line)")
+    ap.add_argument("--no-qk", action="store_true",
+                    help="skip the QK-norm, RMSNorm and MXFP8-quantiser measurements")
+    ap.add_argument("--norms", "--aux", dest="norms", action="store_true",
+                    help="only the QK-norm, RMSNorm and MXFP8-quantiser measurements "
+                         "(one JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="also run a plain device copy of MB megabytes (counter calibration)")
     return ap.parse_args()
@@ -202,7 +204,8 @@ def main():
     if args.norms:
         dev = torch.device("cuda:0")
         print(json.dumps({"qk_norm": qk_norm_bench(B, R, dev, args.steps),
-                          "rms_norm": rms_norm_bench(B, R, dev, args.steps)}), flush=True)
+                          "rms_norm": rms_norm_bench(B, R, dev, args.steps),
+                          "mx_quant": mx_quant_bench(B, R, dev, args.steps)}), flush=True)
         return
 
     hc = args.config
@@ -266,6 +269,7 @@ def main():
     if not args.only and not args.no_qk:
         line["qk_norm"] = qk_norm_bench(B, R, dev, args.steps)
         line["rms_norm"] = rms_norm_bench(B, R, dev, args.steps)
+        line["mx_quant"] = mx_quant_bench(B, R, dev, args.steps)
     if args.copy_calibration:
         # a plain copy of known size, so hardware byte counters can be scaled
         n = args.copy_calibration * (1 << 20)
@@ -342,6 +346,39 @@ def rms_norm_bench(B, roof, dev, steps):
     us = t0.elapsed_time(t1) * 1e3 / n
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"workload": f"row RMSNorm, bf16, T={T}, d={d}, out of place",
+            "us_per_launch": us, "algorithmic_bytes_per_launch": nbytes, "GB/s": gbs,
+            "frac_of_hbm_peak": gbs * 1e9 / roof.HBM_BYTES_PER_S, "cache_guard_copies": copies}
+
+
+def mx_quant_bench(B, roof, dev, steps):
+    """MXFP8 quantisation of the E=256 top-8 layer's activations at prefill
+    (16384 tokens x d = 7168, bf16): HBM-bound, algorithmic bytes = x read
+    once, the codes and scale bytes written once.  Launches cycle through
+    copies so that one cycle moves >= 1 GiB (Infinity-Cache guard)."""
+    import torch
+    from workloads.mxq import make_mx_rows
+    rows, n = 16384, 7168
+    nbytes = rows * n * 2 + rows * n + rows * n // 32
+    copies = max(1, min(MAX_REPLICAS, -(-GUARD_BYTES // nbytes)))
+    sets = []
+    for i in range(copies):
+        x = make_mx_rows(rows, n, "bf16", seed=i, device=dev)
+        sets.append((x, torch.empty((rows, n), dtype=torch.uint8, device=dev),
+                     torch.empty((rows, n // 32), dtype=torch.uint8, device=dev)))
+    for i in range(max(3, copies)):
+        B.quantize_mxfp8(*sets[i % copies])
+    torch.cuda.synchronize()
+    cnt = max(steps, 20) * copies
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(cnt):
+        B.quantize_mxfp8(*sets[i % copies])
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / cnt
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": f"MXFP8 quantisation (32-element blocks), bf16 in, rows={rows}, n={n}",
             "us_per_launch": us, "algorithmic_bytes_per_launch": nbytes, "GB/s": gbs,
             "frac_of_hbm_peak": gbs * 1e9 / roof.HBM_BYTES_PER_S, "cache_guard_copies": copies}
 

@@ -307,6 +307,32 @@ int moe_qk_norm(void* q, void* k, const void* q_weight, const void* k_weight, in
                 int n_q_heads, int n_k_heads, int head_dim, int dtype, float weight_bias,
                 float eps, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * moe_quantize_mxfp8 — MXFP8 quantisation of activation rows.  "CuTeDSL at
+ * Perplexity", section on Blackwell support: the block-scaled formats share
+ * one scale per block of 32 consecutive elements, found from the block's
+ * absmax.  With the OCP MX rule for MXFP8, for every block of 32 consecutive
+ * elements of a row:
+ *   s     = floor(log2(max |x|)) - 8, at least -127 (an all-zero block: -127)
+ *   code  = E4M3 ("fn") of x * 2^-s, rounded to nearest with ties to even,
+ *           magnitudes above 448 saturated to 448, the sign bit that of x
+ *   scale = s + 127 (an E8M0 byte, 0..246)
+ * so that x ~ e4m3(code) * 2^(scale - 127), the MOE_MXFP8 encoding with the
+ * blocks along the row.
+ *
+ *   x       [rows, n]     dtype (device)
+ *   codes   [rows, n]     bytes (device, written)
+ *   scales  [rows, n/32]  bytes (device, written)
+ *   dtype   MOE_BF16 or MOE_F32
+ * Limits: rows >= 0, n > 0 (else MOE_ERR_INVALID); n % 32 == 0 and dtype as
+ * above (else MOE_ERR_UNSUPPORTED); the three regions must not overlap
+ * (MOE_ERR_INVALID).  Inputs must be finite (a NaN or infinity gives
+ * unspecified codes and scale for its block).  One launch, no workspace;
+ * x is read once.
+ * ------------------------------------------------------------------------- */
+int moe_quantize_mxfp8(const void* x, int rows, int n, int dtype, void* codes, void* scales,
+                       void* stream);
+
 /* Static description of a status code (host). */
 const char* moe_status_string(int status);
 

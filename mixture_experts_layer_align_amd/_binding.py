@@ -20,8 +20,8 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8 = 0, 1, 2, 3, 4
 MOE_BLOCK_M_MAX = 256
 
 EXPORTED = ["moe_align_capacity", "moe_route", "moe_align", "moe_forward", "moe_forward_traced",
-            "moe_forward_noalloc", "moe_rms_norm", "moe_qk_norm", "moe_status_string",
-            "moe_abi_version"]
+            "moe_forward_noalloc", "moe_rms_norm", "moe_qk_norm", "moe_quantize_mxfp8",
+            "moe_status_string", "moe_abi_version"]
 
 _c = ctypes
 _vp = _c.c_void_p
@@ -89,6 +89,8 @@ def load():
     lib.moe_qk_norm.argtypes = [_vp, _vp, _vp, _vp, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                 _c.c_int, _c.c_float, _c.c_float, _vp]
     lib.moe_status_string.restype = _c.c_char_p
+    lib.moe_quantize_mxfp8.restype = _c.c_int
+    lib.moe_quantize_mxfp8.argtypes = [_vp, _c.c_int, _c.c_int, _c.c_int, _vp, _vp, _vp]
     lib.moe_status_string.argtypes = [_c.c_int]
     lib.moe_abi_version.restype = _c.c_int
     lib.moe_abi_version.argtypes = []
@@ -175,6 +177,28 @@ def align(topk_ids: torch.Tensor, E: int, block_m: int, stream=None):
     ws, nb = _workspace(call, dev)
     _check(call(_ptr(ws), _c.byref(nb)), "moe_align")
     return out
+
+
+def quantize_mxfp8(x: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                   scales: Optional[torch.Tensor] = None, stream=None):
+    """MXFP8 codes (uint8 [rows, n]) and E8M0 scale bytes (uint8 [rows, n/32])
+    of x [rows, n] (bf16 or fp32, blocks of 32 along the row).  Returns
+    (codes, scales)."""
+    rows, n = x.shape
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if codes is None:
+        codes = torch.empty((rows, n), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, n // 32), dtype=torch.uint8, device=x.device)
+    for t in (codes, scales):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("codes and scales: contiguous uint8")
+    if codes.shape != (rows, n) or scales.shape != (rows, n // 32):
+        raise ValueError("codes [rows, n] and scales [rows, n/32]")
+    _check(load().moe_quantize_mxfp8(_ptr(x), rows, n, act_code(x.dtype), _ptr(codes),
+                                     _ptr(scales), _stream(stream)), "moe_quantize_mxfp8")
+    return codes, scales
 
 
 def rms_norm(x: torch.Tensor, weight: torch.Tensor, out: Optional[torch.Tensor] = None,

@@ -12,7 +12,7 @@ OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libmoe.so")
 
 SOURCES = ["moe_api.hip", "router_gemm.hip", "expert_gemm_stream.hip", "expert_gemm_tiled.hip",
-           "route_align.hip", "combine.hip", "rms_norm.hip"]
+           "route_align.hip", "combine.hip", "rms_norm.hip", "mx_quant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

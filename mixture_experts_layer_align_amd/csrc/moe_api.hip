@@ -326,6 +326,26 @@ int moe_rms_norm(const void* x, const void* weight, void* out, int T, int d, int
   return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
+int moe_quantize_mxfp8(const void* x, int rows, int n, int dtype, void* codes, void* scales,
+                       void* stream) {
+  if (rows < 0 || n <= 0) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (n % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return MOE_ERR_INVALID;
+  // the three regions must not overlap
+  const int64_t elems = (int64_t)rows * n;
+  const char* r[3] = {static_cast<const char*>(x), static_cast<const char*>(codes),
+                      static_cast<const char*>(scales)};
+  const int64_t len[3] = {elems * (dtype == MOE_BF16 ? 2 : 4), elems, elems / 32};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (r[i] < r[j] + len[j] && r[j] < r[i] + len[i]) return MOE_ERR_INVALID;
+  const hipError_t e = launch_mx_quant(dtype == MOE_BF16 ? ACT_BF16 : ACT_F32, x, codes, scales,
+                                       rows, n, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
 int moe_route(const void* x, const void* w_router, const float* logit_bias, int T, int d, int E,
               int k, int act_dtype, float* logits, int32_t* topk_ids, float* topk_w,
               void* workspace, size_t* workspace_bytes, void* stream) {

@@ -188,4 +188,9 @@ constexpr int RMS_MAX_ROW_BYTES = 32768;
 hipError_t launch_rms_norm(int act_dtype, const void* x, const void* w, void* y, int T, int d,
                            float weight_bias, float eps, hipStream_t st);
 
+// MXFP8 codes [rows][n] and E8M0 scale bytes [rows][n/32] of x [rows][n]
+// (bf16 or fp32, n % 32 == 0).
+hipError_t launch_mx_quant(int act_dtype, const void* x, void* codes, void* scales, int64_t rows,
+                           int n, hipStream_t st);
+
 }  // namespace moe

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     src = open(os.path.join(ROOT, "include", "libmoe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -231,3 +231,24 @@ def test_rms_norm_validation_on_host():
                             None) == B.MOE_ERR_INVALID
     # an empty batch is valid and launches nothing
     assert lib.moe_rms_norm(None, None, None, 0, 2048, B.MOE_BF16, 0.0, 1e-6, None) == B.MOE_OK
+
+
+def test_quantize_mxfp8_validation_on_host():
+    lib = B.load()
+    vp = ctypes.c_void_p
+    X, C, S = vp(1 << 20), vp(1 << 24), vp(1 << 28)
+    # n not a multiple of 32, or a dtype other than bf16/fp32: unsupported
+    assert lib.moe_quantize_mxfp8(X, 4, 48, B.MOE_BF16, C, S, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_mxfp8(X, 4, 64, B.MOE_FP8_E4M3, C, S, None) == B.MOE_ERR_UNSUPPORTED
+    # negative rows, n <= 0, missing pointers
+    assert lib.moe_quantize_mxfp8(X, -1, 64, B.MOE_BF16, C, S, None) == B.MOE_ERR_INVALID
+    assert lib.moe_quantize_mxfp8(X, 4, 0, B.MOE_BF16, C, S, None) == B.MOE_ERR_INVALID
+    assert lib.moe_quantize_mxfp8(None, 4, 64, B.MOE_BF16, C, S, None) == B.MOE_ERR_INVALID
+    assert lib.moe_quantize_mxfp8(X, 4, 64, B.MOE_BF16, C, None, None) == B.MOE_ERR_INVALID
+    # overlapping regions: codes inside x, scales inside codes
+    assert lib.moe_quantize_mxfp8(X, 4, 64, B.MOE_BF16, vp((1 << 20) + 100), S,
+                                  None) == B.MOE_ERR_INVALID
+    assert lib.moe_quantize_mxfp8(X, 4, 64, B.MOE_F32, C, vp((1 << 24) + 255),
+                                  None) == B.MOE_ERR_INVALID
+    # no rows: valid, nothing enqueued
+    assert lib.moe_quantize_mxfp8(None, 0, 64, B.MOE_BF16, None, None, None) == B.MOE_OK
