@@ -377,19 +377,26 @@ __device__ int hist_wave_prefix(int* hist, int E) {
 
 // counts/offsets known (in LDS): write counts, offsets, padding -1 slots,
 // block_expert and, if asked for, the tiled GEMM's row list.  Called by every
-// thread of one workgroup (E <= AL_THREADS); sh is scan scratch.
+// thread of one workgroup (E <= AL_THREADS); sh is scan scratch.  PREFILLED:
+// the workgroup already set every slot and block to -1 (prefill_layout,
+// ordered before this by a workgroup barrier), so only the experts' blocks
+// are written here.
+template <bool PREFILLED>
 __device__ void write_layout(const AlignArgs& a, const int* s_counts, const int* s_off, int* sh) {
   const int E = a.E, bm = a.bm;
   for (int e = threadIdx.x; e < E; e += AL_THREADS) {
     a.counts[e] = s_counts[e];
     a.offsets[e] = s_off[e];
-    for (int s = s_off[e] + s_counts[e]; s < s_off[e + 1]; ++s) a.sorted_ids[s] = -1;
+    if (!PREFILLED)
+      for (int s = s_off[e] + s_counts[e]; s < s_off[e + 1]; ++s) a.sorted_ids[s] = -1;
     for (int b = s_off[e] / bm; b < s_off[e + 1] / bm; ++b) a.block_expert[b] = e;
   }
   if (threadIdx.x == 0) a.offsets[E] = s_off[E];
-  for (int64_t s = s_off[E] + threadIdx.x; s < a.cap; s += AL_THREADS) a.sorted_ids[s] = -1;
-  for (int64_t b = s_off[E] / bm + threadIdx.x; b < a.cap / bm; b += AL_THREADS)
-    a.block_expert[b] = -1;
+  if (!PREFILLED) {
+    for (int64_t s = s_off[E] + threadIdx.x; s < a.cap; s += AL_THREADS) a.sorted_ids[s] = -1;
+    for (int64_t b = s_off[E] / bm + threadIdx.x; b < a.cap / bm; b += AL_THREADS)
+      a.block_expert[b] = -1;
+  }
   if (a.tile_rows == nullptr) return;
   // rows of 256 slots; a remainder (128 slots when bm = 128) is a half row
   const int e = threadIdx.x;
@@ -422,6 +429,17 @@ __device__ void write_layout(const AlignArgs& a, const int* s_counts, const int*
   if (threadIdx.x < TILE_COUNTERS) a.tile_counts[2 + threadIdx.x] = 0;
 }
 
+// Every slot of sorted_ids and every block of block_expert to -1, by all
+// threads of a single-workgroup launch, before the routed slots and the
+// experts' blocks are written over them after a workgroup barrier (which
+// waits for these stores): one coalesced pass instead of per-expert padding
+// loops and a tail fill on a few threads.
+__device__ void prefill_layout(const AlignArgs& a) {
+  for (int64_t s = threadIdx.x; s < a.cap; s += blockDim.x) a.sorted_ids[s] = -1;
+  const int64_t nb = a.cap / a.bm;
+  for (int64_t b = threadIdx.x; b < nb; b += blockDim.x) a.block_expert[b] = -1;
+}
+
 __device__ __forceinline__ int ilog2_ceil(int E) {
   int b = 0;
   while ((1 << b) < E) ++b;
@@ -429,7 +447,9 @@ __device__ __forceinline__ int ilog2_ceil(int E) {
 }
 
 // One workgroup aligns all entries (n <= ALIGN_TILE) of `ids` (global or
-// LDS memory); lds holds AL_WAVES * E + 2 * E + 1 + AL_WAVES + 1 ints.
+// LDS memory); lds holds AL_WAVES * E + 2 * E + 1 + AL_WAVES + 1 ints.  The
+// layout arrays must have been prefilled (prefill_layout) by the workgroup;
+// the barriers below order those stores first.
 __device__ void align_one_tile(const AlignArgs& a, const int32_t* ids, int* lds) {
   int* hist = lds;                          // [AL_WAVES][E]
   int* s_counts = hist + AL_WAVES * a.E;    // [E]
@@ -458,7 +478,7 @@ __device__ void align_one_tile(const AlignArgs& a, const int32_t* ids, int* lds)
     a.sorted_ids[pos] = i;
     a.inv_pos[i] = pos;
   }
-  write_layout(a, s_counts, s_off, sh);
+  write_layout<true>(a, s_counts, s_off, sh);
 }
 
 // One wave aligns n <= 64 entries (ids in LDS, E <= 64 * EPL) without the
@@ -466,7 +486,9 @@ __device__ void align_one_tile(const AlignArgs& a, const int32_t* ids, int* lds)
 // entries below it comes from the match mask, the leader of each expert
 // writes the count to LDS, and lane l owns experts EPL*l .. EPL*l + EPL - 1
 // (contiguous, so one wave scan of the lanes' padded sums gives the offsets
-// in expert order).  Same layout as align_one_tile.  cl: E ints of LDS.
+// in expert order).  Same layout as align_one_tile (prefilled the same way,
+// the prefill ordered before this wave's stores by a workgroup barrier).
+// cl: E ints of LDS.
 template <int EPL>
 __device__ void align_one_wave(const AlignArgs& a, const int32_t* ids, int* cl) {
   const int lane = threadIdx.x & 63;
@@ -513,12 +535,9 @@ __device__ void align_one_wave(const AlignArgs& a, const int32_t* ids, int* cl) 
     if (ee >= E) continue;
     a.counts[ee] = c[j];
     a.offsets[ee] = off[j];
-    for (int s = off[j] + c[j]; s < off[j] + pad[j]; ++s) a.sorted_ids[s] = -1;
     for (int b = off[j] / bm; b < (off[j] + pad[j]) / bm; ++b) a.block_expert[b] = ee;
   }
   if (lane == 0) a.offsets[E] = total;
-  for (int64_t s = total + lane; s < a.cap; s += 64) a.sorted_ids[s] = -1;
-  for (int64_t b = total / bm + lane; b < a.cap / bm; b += 64) a.block_expert[b] = -1;
   // the entry's expert offset, from its owner lane
   int oe = 0;
 #pragma unroll
@@ -534,6 +553,7 @@ __device__ void align_one_wave(const AlignArgs& a, const int32_t* ids, int* cl) 
 
 __global__ __launch_bounds__(AL_THREADS) void k_align_single(const AlignArgs a) {
   extern __shared__ int lds[];
+  prefill_layout(a);
   align_one_tile(a, a.ids, lds);
 }
 
@@ -624,6 +644,9 @@ __global__ __launch_bounds__(NT) void k_route_align_small(
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int E = a.E, k = a.k;
+  // every wave's share of the -1 layout first: the stores drain while the
+  // routing waits on its loads (the barrier after routing orders them)
+  prefill_layout(a);
   // the narrow workgroup (fewer waves, more registers each) loads every
   // plane in one batch: one memory round trip instead of two at V = 4
   constexpr int NBS = NT < AL_THREADS ? ROUTER_MAX_SPLIT : 0;
@@ -763,7 +786,7 @@ __global__ __launch_bounds__(AL_THREADS) void k_align_scatter(const AlignArgs a)
       a.inv_pos[i] = pos;
     }
   }
-  if (blockIdx.x == 0) write_layout(a, s_counts, s_off, sh);
+  if (blockIdx.x == 0) write_layout<false>(a, s_counts, s_off, sh);
 }
 
 int64_t align_workspace_bytes(int n, int E) {
