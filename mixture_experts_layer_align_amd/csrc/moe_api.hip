@@ -458,12 +458,15 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
     // MX weights (a scale per 32 k to fetch and apply) stream faster with two
     // workgroups per compute unit when K is split for few experts: split as
     // if the chip had twice the units (E=256 top-8 T=1: MXFP8 0.124 -> 0.115
-    // ms, MXFP4 0.086 -> 0.083; fp8 measured slower that way and keeps one)
+    // ms, MXFP4 0.086 -> 0.083); so do fp8 down GEMMs (their bf16-pair h
+    // doubles the MFMAs per weight byte: E=256 top-8 T=1 down 44 -> 35 µs;
+    // four per unit: 43 µs), while the fp8 gate|up keeps one (two: 50 -> 52)
     const int wmul = (wdt == W_MXFP8 || wdt == W_FP4) ? 2 : 1;
+    const int wmul_dn = wdt == W_BF16 ? 1 : 2;
     gu_chunk = choose_kchunk_balanced(gu_items, d, kstep, &gu_split, wmul * SPLIT_BELOW,
                                       MIN_SPLIT_STEPS, 64, wmul * cus);
-    dn_chunk = choose_kchunk_balanced(dn_items, dff, kstep, &dn_split, wmul * SPLIT_BELOW,
-                                      MIN_SPLIT_STEPS, 64, wmul * cus);
+    dn_chunk = choose_kchunk_balanced(dn_items, dff, kstep, &dn_split, wmul_dn * SPLIT_BELOW,
+                                      MIN_SPLIT_STEPS, 64, wmul_dn * cus);
     // bf16 weights stream fastest with one workgroup per compute unit; fp8
     // weights (twice the math per byte) need the latency hiding of several
     // workgroups per compute unit and keep one workgroup per item
