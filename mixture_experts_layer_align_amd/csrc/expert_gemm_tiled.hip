@@ -629,12 +629,21 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
         for (int r = 0; r < 4; ++r) sc[ni][r] = __uint_as_float(v[r]);
       }
     }
+    // The wave's 128 x 128 block goes through LDS (the ring is idle once
+    // every wave has read its last fragments): a direct 8-byte store per
+    // block writes 32 bytes into each of 16 rows, and those scattered
+    // stores cost the short-K down GEMMs 10-25 % of their time; read back
+    // row-wise, one instruction stores 4 whole 256-byte row segments.
+    // Staged rows are 272 bytes apart, so the 8-byte writes of a half-wave
+    // hit 64 distinct banks.
+    constexpr int RS = 272;
+    static_assert(4 * 128 * RS <= Ring<WT>::LDS_BYTES, "staging fits the ring");
+    char* stage = lds + wave * 128 * RS;
+    __syncthreads();  // every wave has read its last fragments
     const int vrows = n_valid - lrow0;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       if (mi * 16 >= vrows) continue;  // padding slot
-      uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + ks * p.out_split_stride +
-                      (int64_t)(p0 + lrow0 + mi * 16) * p.out_ld + c0;
 #pragma unroll
       for (int ni = 0; ni < 8; ++ni) {
         float v[4];
@@ -644,8 +653,20 @@ __device__ __forceinline__ int run_tile(const StreamGemmArgs& p, char* lds, uint
           if constexpr (WT == W_FP8) v[r] *= sc[ni][r];
         }
         const u32x2 o = {pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(dst + ni * 16) = o;
+        *reinterpret_cast<u32x2*>(stage + (mi * 16 + lm) * RS + ni * 32 + lg * 8) = o;
       }
+    }
+    // routed rows of the wave's block (a prefix: routed slots come first)
+    const int wrows = min(128, n_valid - wm * 128);
+    char* gdst = reinterpret_cast<char*>(p.out) +
+                 (ks * p.out_split_stride + (int64_t)(p0 + wm * 128) * p.out_ld + ntw * TBN +
+                  wn * 128) * 2;
+#pragma unroll 4
+    for (int j = 0; j < 32; ++j) {
+      const int r = 4 * j + (lane >> 4);
+      if (r < wrows)
+        *reinterpret_cast<u32x4*>(gdst + (int64_t)r * p.out_ld * 2 + (lane & 15) * 16) =
+            *reinterpret_cast<const u32x4*>(stage + r * RS + (lane & 15) * 16);
     }
   }
   return claimed;
