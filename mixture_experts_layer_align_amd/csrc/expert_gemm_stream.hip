@@ -40,7 +40,7 @@
 //     gate|up that next kernel is the down GEMM itself: each of its items
 //     first adds the partials of its rows and k-range and applies SiLU*up
 //     (one launch fewer; the prologue lengthens the down kernel by 3-5 µs,
-//     about what the separate reduce kernel and its launch gap took);
+//     about what a separate reduce launch and its gap cost);
 //   * the epilogue runs on the fp32 accumulators before the single store:
 //     SiLU(gate) * up for the concatenated gate|up weight ("La fusion de
 //     noyaux", section 4.2, GEMM + epilogue and the SwiGLU concatenation), and
