@@ -17,10 +17,17 @@ CASES = [
      300),
     (LayerShape(302, "graph-mx", E=16, k=4, d=512, d_ff=256, act="bf16", wdt="mxfp4", seed=8),
      24),
+    # two tokens, long K: gate|up splits K and the down GEMM forms h from
+    # the partials
+    (LayerShape(303, "graph-fold", E=16, k=4, d=1024, d_ff=256, act="bf16", wdt="bf16", seed=9),
+     2),
+    (LayerShape(304, "graph-fold-fp8", E=16, k=4, d=1024, d_ff=256, act="bf16", wdt="fp8",
+                seed=10), 2),
 ]
 
 
-@pytest.mark.parametrize("sh,T", CASES, ids=["decode-bf16", "tiled-bf16", "mxfp4"])
+@pytest.mark.parametrize("sh,T", CASES,
+                         ids=["decode-bf16", "tiled-bf16", "mxfp4", "fold-bf16", "fold-fp8"])
 def test_graph_replays_match_eager(sh, T):
     print(f"graph replay {sh.name} T={T}", flush=True)
     layer = make_layer(sh, T, "cuda")
