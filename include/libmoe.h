@@ -28,7 +28,9 @@
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless stated otherwise; arrays are dense,
- *     row-major, and 16-byte aligned.  `stream` is a hipStream_t (NULL: the
+ *     row-major, and 16-byte aligned (routing arrays of int32/fp32 and the
+ *     logit bias need only 4, MXFP8 codes 8 and their scale bytes 4); a
+ *     misaligned pointer returns MOE_ERR_INVALID.  `stream` is a hipStream_t (NULL: the
  *     default stream).  All work is enqueued on `stream`; the library never
  *     synchronises, never allocates or frees device memory and never prints.
  *     Outputs are valid once the stream reaches that point.

@@ -213,6 +213,12 @@ hipError_t run_router(RouterPlan& r, int act, float* partial, const float* bias,
 
 // Shapes and dtypes; data pointers are checked only when work is enqueued
 // (a workspace query needs none).
+// p is not NULL and not a multiple of a bytes: the 16-byte vector loads and
+// stores (and direct-to-LDS loads) of the kernels need their arrays aligned.
+bool misaligned(const void* p, uintptr_t a) {
+  return p != nullptr && reinterpret_cast<uintptr_t>(p) % a != 0;
+}
+
 int validate_route(int T, int d, int E, int k, int act) {
   if (T < 0 || d <= 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID;
   if (k > E || E > MOE_MAX_EXPERTS) return MOE_ERR_INVALID;
@@ -300,6 +306,9 @@ int moe_qk_norm(void* q, void* k, const void* q_weight, const void* k_weight, in
   if (T == 0 || n_q_heads + n_k_heads == 0) return MOE_OK;
   if (n_q_heads > 0 && (q == nullptr || q_weight == nullptr)) return MOE_ERR_INVALID;
   if (n_k_heads > 0 && (k == nullptr || k_weight == nullptr)) return MOE_ERR_INVALID;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(q_weight, 16) ||
+      misaligned(k_weight, 16))
+    return MOE_ERR_INVALID;
   const hipError_t e =
       launch_qk_norm(dtype == MOE_BF16 ? ACT_BF16 : ACT_F32, q, k, q_weight, k_weight, T,
                      n_q_heads, n_k_heads, head_dim, weight_bias, eps,
@@ -316,6 +325,7 @@ int moe_rms_norm(const void* x, const void* weight, void* out, int T, int d, int
   if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(weight_bias)) return MOE_ERR_INVALID;
   if (T == 0) return MOE_OK;
   if (x == nullptr || weight == nullptr || out == nullptr) return MOE_ERR_INVALID;
+  if (misaligned(x, 16) || misaligned(weight, 16) || misaligned(out, 16)) return MOE_ERR_INVALID;
   // out is x itself or does not overlap it
   const char* xb = static_cast<const char*>(x);
   const char* ob = static_cast<const char*>(out);
@@ -333,6 +343,7 @@ int moe_quantize_mxfp8(const void* x, int rows, int n, int dtype, void* codes, v
   if (n % 32 != 0) return MOE_ERR_UNSUPPORTED;
   if (rows == 0) return MOE_OK;
   if (x == nullptr || codes == nullptr || scales == nullptr) return MOE_ERR_INVALID;
+  if (misaligned(x, 16) || misaligned(codes, 8) || misaligned(scales, 4)) return MOE_ERR_INVALID;
   // the three regions must not overlap
   const int64_t elems = (int64_t)rows * n;
   const char* r[3] = {static_cast<const char*>(x), static_cast<const char*>(codes),
@@ -360,6 +371,9 @@ int moe_route(const void* x, const void* w_router, const float* logit_bias, int 
   if (rc != MOE_OK || query || T == 0) return rc;
   if (x == nullptr || w_router == nullptr || topk_ids == nullptr || topk_w == nullptr)
     return MOE_ERR_INVALID;
+  if (misaligned(x, 16) || misaligned(w_router, 16) || misaligned(logit_bias, 4) ||
+      misaligned(logits, 4) || misaligned(topk_ids, 4) || misaligned(topk_w, 4))
+    return MOE_ERR_INVALID;
   int kidx = 0;
   hipError_t e = run_router(r, act, partial, logit_bias, T, E, k, logits, topk_ids, topk_w,
                             static_cast<hipStream_t>(stream), nullptr, &kidx);
@@ -381,6 +395,9 @@ int moe_align(const int32_t* topk_ids, int T, int E, int k, int block_m, int32_t
   if (T == 0) return MOE_OK;
   if (topk_ids == nullptr || expert_counts == nullptr || padded_offsets == nullptr ||
       sorted_ids == nullptr || inv_pos == nullptr || block_expert == nullptr)
+    return MOE_ERR_INVALID;
+  if (misaligned(topk_ids, 4) || misaligned(expert_counts, 4) || misaligned(padded_offsets, 4) ||
+      misaligned(sorted_ids, 4) || misaligned(inv_pos, 4) || misaligned(block_expert, 4))
     return MOE_ERR_INVALID;
   AlignArgs a{};
   a.ids = topk_ids;
@@ -519,6 +536,17 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   if (T == 0) return MOE_OK;
   if (x == nullptr || out == nullptr || L->w_router == nullptr || L->w_gate_up == nullptr ||
       L->w_down == nullptr || out == x)
+    return MOE_ERR_INVALID;
+  if (misaligned(x, 16) || misaligned(out, 16) || misaligned(L->w_router, 16) ||
+      misaligned(L->w_gate_up, 16) || misaligned(L->w_down, 16) ||
+      misaligned(L->scale_gate_up, 16) || misaligned(L->scale_down, 16) ||
+      misaligned(L->logit_bias, 4))
+    return MOE_ERR_INVALID;
+  if (routing != nullptr &&
+      (misaligned(routing->logits, 4) || misaligned(routing->topk_ids, 4) ||
+       misaligned(routing->topk_w, 4) || misaligned(routing->expert_counts, 4) ||
+       misaligned(routing->padded_offsets, 4) || misaligned(routing->sorted_ids, 4) ||
+       misaligned(routing->inv_pos, 4)))
     return MOE_ERR_INVALID;
 
   // routing views the caller asked for are written in place

@@ -252,3 +252,52 @@ def test_quantize_mxfp8_validation_on_host():
                                   None) == B.MOE_ERR_INVALID
     # no rows: valid, nothing enqueued
     assert lib.moe_quantize_mxfp8(None, 0, 64, B.MOE_BF16, None, None, None) == B.MOE_OK
+
+
+def test_misaligned_pointers_are_refused_on_host():
+    """Each entry point refuses, before any launch, an array whose address is
+    not a multiple of its kernels' widest access (16 bytes for activations and
+    weights, 4 for the int32/fp32 routing arrays, 8 for MXFP8 codes)."""
+    lib = B.load()
+    vp = ctypes.c_void_p
+    A = 1 << 20                                            # an aligned fake address
+    # rms norm: x, weight and out need 16 bytes
+    for args in ((A + 8, A, 4 * A), (A, A + 4, 4 * A), (A, A, 4 * A + 2)):
+        assert lib.moe_rms_norm(vp(args[0]), vp(args[1]), vp(args[2]), 4, 2048, B.MOE_BF16, 0.0,
+                                1e-6, None) == B.MOE_ERR_INVALID
+    # qk norm: q, k and their weights
+    assert _qk(q=A + 8, k=2 * A, wq=3 * A, wk=4 * A) == B.MOE_ERR_INVALID
+    assert _qk(q=A, k=2 * A + 4, wq=3 * A, wk=4 * A) == B.MOE_ERR_INVALID
+    assert _qk(q=A, k=2 * A, wq=3 * A + 2, wk=4 * A) == B.MOE_ERR_INVALID
+    # quantiser: x 16, codes 8, scales 4
+    X, C, S = 1 << 20, 1 << 24, 1 << 28
+    for x, c, s in ((X + 8, C, S), (X, C + 4, S), (X, C, S + 2)):
+        assert lib.moe_quantize_mxfp8(vp(x), 4, 64, B.MOE_BF16, vp(c), vp(s),
+                                      None) == B.MOE_ERR_INVALID
+    # route: x and the router weights 16, the fp32/int32 outputs 4
+    ws = vp(1 << 30)
+    n = ctypes.c_size_t(1 << 20)
+    for x, w, ids, tw in ((A + 8, 2 * A, 3 * A, 4 * A), (A, 2 * A + 8, 3 * A, 4 * A),
+                          (A, 2 * A, 3 * A + 2, 4 * A), (A, 2 * A, 3 * A, 4 * A + 1)):
+        assert lib.moe_route(vp(x), vp(w), None, 4, 128, 8, 2, B.MOE_BF16, None, vp(ids), vp(tw),
+                             ws, ctypes.byref(n), None) == B.MOE_ERR_INVALID
+    # align: every int32 array 4
+    for bad in range(6):
+        ptrs = [vp(A * (i + 1) + (2 if i == bad else 0)) for i in range(6)]
+        n = ctypes.c_size_t(1 << 20)
+        assert lib.moe_align(ptrs[0], 4, 8, 2, 32, *ptrs[1:], ws, ctypes.byref(n),
+                             None) == B.MOE_ERR_INVALID
+    # forward: x, out, the three weight arrays and the fp8 scales 16
+    _, need = _fwd(_layer(), T=64)
+    for kw, x, out in (({}, A + 8, 2 * A), ({}, A, 2 * A + 4)):
+        L = _layer(**kw)
+        assert _fwd(L, T=64, ws=vp(1 << 30), nbytes=need, x=x, out=out)[0] == B.MOE_ERR_INVALID
+    for field in ("w_router", "w_gate_up", "w_down"):
+        L = _layer()
+        L.w_router, L.w_gate_up, L.w_down = 3 * A, 4 * A, 5 * A
+        setattr(L, field, getattr(L, field) + 8)
+        assert _fwd(L, T=64, ws=vp(1 << 30), nbytes=need, x=A, out=2 * A)[0] == B.MOE_ERR_INVALID
+    L = _layer(wdt=B.MOE_FP8_E4M3, sgu=6 * A + 4, sdn=7 * A)
+    L.w_router, L.w_gate_up, L.w_down = 3 * A, 4 * A, 5 * A
+    _, need8 = _fwd(L, T=64)
+    assert _fwd(L, T=64, ws=vp(1 << 30), nbytes=need8, x=A, out=2 * A)[0] == B.MOE_ERR_INVALID
