@@ -105,15 +105,22 @@ struct DTr<W_F32> {
   static constexpr int ESIZE = 4;
 };
 
+#ifndef STREAM_HV2_STAGES
+#define STREAM_HV2_STAGES 8
+#endif
 // Load-ring stages per wave.  bf16: two — with fewer requests outstanding
 // HBM serves the weight stream faster (more stages measured slower on gfx950).
 // fp8: four — its heavier per-stage math needs the deeper ring, and the
 // larger LDS footprint keeps two workgroups per compute unit.  MXFP4: eight
 // stages of 4 KB (the same bytes in flight as fp8; with four its waves spent
 // half their time waiting for loads).
-template <int WT>
+//
+// Two-half blocks (HV = 2) use more than 256 registers per wave, so one
+// workgroup runs per compute unit: eight stages (128 KB) keep as many weight
+// bytes in flight per unit as two one-half workgroups with four each.
+template <int WT, int HV = 1>
 constexpr int stages_of() {
-  return WT == W_BF16 ? 2 : WT == W_FP4 ? 8 : 4;  // fp8 and MXFP8: 4
+  return HV == 2 ? STREAM_HV2_STAGES : WT == W_BF16 ? 2 : WT == W_FP4 ? 8 : 4;  // fp8, MXFP8: 4
 }
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
@@ -151,10 +158,10 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
 }  // namespace
 
 // h[p, k] = SiLU(sum_s g_s[p, k]) * sum_s u_s[p, k] for the routed rows p of
-// the block at p0 (bit r of `routed`: row p0 + r) and k in [kb, ke), splits
+// the 32 rows at p0 (bit r of `routed`: row p0 + r) and k in [kb, ke), splits
 // added in order, from the gate|up k-split partial sums; stored where the
-// item's main loop reads its rows (as a bf16 pair when HILO).  All 128
-// threads take part: 8 consecutive columns of one routed row per thread and
+// item's main loop reads its rows (as a bf16 pair when HILO).  The 128
+// threads of those rows (tid 0-127) take part: 8 consecutive columns of one routed row per thread and
 // pass, the loads of up to FOLD_SPLITS splits in flight at once (the partials
 // come from other dies' L2 or HBM: one round trip per group of splits).  The
 // workgroups of the block's other n-tiles write the same values to the same
@@ -162,11 +169,11 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
 constexpr int FOLD_SPLITS = 8;
 template <int ACT, bool HILO>
 __device__ __forceinline__ void fold_split_silu(const StreamGemmArgs& p, uint32_t routed, int p0,
-                                                int kb, int ke) {
+                                                int kb, int ke, int tid) {
   constexpr int ASZ = (ACT == ACT_BF16) ? 2 : 4;
   const int K = p.K;  // gate|up's d_ff: up columns start at K
   const int per_row = (ke - kb) / 8;
-  for (int u = threadIdx.x; u < STREAM_BM * per_row; u += 128) {
+  for (int u = tid; u < STREAM_BM * per_row; u += 128) {
     const int r = u / per_row;
     if (!((routed >> r) & 1u)) continue;
     const int c = kb + 8 * (u - r * per_row);
@@ -212,11 +219,23 @@ __device__ __forceinline__ void fold_split_silu(const StreamGemmArgs& p, uint32_
   }
 }
 
-// One item = (32-row block, n-tile, k-split) of the launch.  HILO: the token
+// One item = (block, n-tile, k-split) of the launch.  HILO: the token
 // rows come as bf16 pairs (p.a high halves, p.a_lo low halves) and every
 // weight fragment is applied to both, which carries h into the down GEMM at
 // 16 significant bits instead of 8.
-template <int ACT, int WT, int EPI, bool HILO>
+//
+// HV = 1: one 32-row block per item, two waves (one per slab), each wave
+// with a load ring of its own and no workgroup barrier in the k-loop.  HV = 2
+// (gate|up with fp8 weights): a pair of consecutive blocks of one expert per
+// item, four waves; wave (slab, half) applies its slab's weights to the rows
+// of block `half` of the pair.  The two waves of a slab share one ring: each
+// issues half of every stage's weight rows (the same lane addresses either
+// would use), and one workgroup barrier per k-step, after each wave's own
+// vmcnt wait, publishes the landed stage and retires the stage read in the
+// previous step, which is then refilled.  An expert's weights then stream
+// once per two blocks; a half with no routed row loads only its share of the
+// weights.
+template <int ACT, int WT, int EPI, bool HILO, int HV>
 __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32x4* lds) {
   using Tr = DTr<WT>;
   constexpr int CPL = Tr::CPL;
@@ -226,17 +245,22 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
   constexpr int NV = 4 * CPL;     // contiguous output columns per lane
   constexpr int ASZ = (ACT == ACT_BF16) ? 2 : 4;
   constexpr int XK = (ACT == ACT_BF16) ? 8 : 4;  // k-values per lane per token fragment
-  constexpr int S = stages_of<WT>();
+  constexpr int S = stages_of<WT, HV>();
   constexpr bool MX = WT == W_FP4 || WT == W_MXFP8;  // E8M0 block scales
   constexpr bool PACK = WT == W_FP4;                  // two codes per byte along K
   static_assert(!HILO || (ACT == ACT_BF16 && WT != W_F32), "bf16 pairs");
-  // vector-memory ops per stage: weight rows + 2 token loads (4 with HILO)
-  // (+ the MX scales)
-  constexpr int PER = RPL + (HILO ? 4 : 2) + (MX ? 1 : 0);
+  static_assert(HV == 1 || HV == 2, "one or two 32-row halves");
+  static_assert(RPL % HV == 0, "the halves split a stage's weight rows");
+  constexpr int RPW = RPL / HV;  // weight rows this wave loads per stage
+  // vector-memory ops per stage: the wave's weight rows + 2 token loads (4
+  // with HILO) (+ the MX scales)
+  constexpr int PER = RPW + (HILO ? 4 : 2) + (MX ? 1 : 0);
   static_assert((S - 1) * PER <= 63, "vmcnt field");
+  static_assert(HV == 1 || S >= 3, "a shared ring keeps a stage in flight past the barrier");
 
   const int lane = threadIdx.x & 63;
-  const int slab = threadIdx.x >> 6;
+  const int slab = HV == 1 ? (int)(threadIdx.x >> 6) : (int)(threadIdx.x >> 6) & 1;
+  const int half = HV == 1 ? 0 : (int)(threadIdx.x >> 7);
   const int li = lane & 15;  // MFMA column within a 16-group (token row)
   const int lg = lane >> 4;  // k group
 
@@ -246,7 +270,16 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
   const int mb = id / p.n_tiles;
   const int e = p.block_expert[mb];
   if (e < 0) return;  // whole workgroup: a block past the routed rows
-  const int p0 = mb * STREAM_BM;
+  // HV = 2: the expert's blocks pair up from its first one; the item of a
+  // pair's second block returns (the first covers it), and a last block
+  // without a partner leaves the second half empty
+  bool half_ok = true;
+  if constexpr (HV == 2) {
+    const int first = p.expert_offsets[e] / STREAM_BM;
+    if ((mb - first) & 1) return;  // whole workgroup
+    half_ok = half == 0 || mb + 1 < p.expert_offsets[e + 1] / STREAM_BM;
+  }
+  const int p0 = (mb + half) * STREAM_BM;
 
   // -------------------------------------------------------- token rows
   const char* arow[2];
@@ -255,7 +288,7 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int prow = p0 + 16 * q + li;
-    const int sid = p.sorted_ids[prow];
+    const int sid = half_ok ? p.sorted_ids[prow] : -1;
     rvalid[q] = sid >= 0;
     int64_t src = 0;  // invalid rows read row 0 (in bounds) and are zeroed
     if (rvalid[q]) src = (p.a_mode == A_GATHER) ? sid / p.topk : prow;
@@ -263,6 +296,9 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
     alrow[q] = HILO ? reinterpret_cast<const char*>(p.a_lo) + src * p.a_ld * ASZ : nullptr;
   }
   const bool use_q1 = ballot(rvalid[1]) != 0;
+  // the half has a routed row (its row 0 is then one: an expert's routed
+  // slots come first in its range); one half: always
+  const bool live = HV == 1 || ballot(rvalid[0]) != 0;
 
   // -------------------------------------------------------- weight columns
   int wcol, ocol;  // this lane's first weight column; first output column
@@ -296,7 +332,7 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
       // lanes 0-15 hold rows 0-15 (q = 0) and 16-31 (q = 1)
       const uint32_t routed = (uint32_t)(ballot(rvalid[0]) & 0xFFFFu) |
                               ((uint32_t)(ballot(rvalid[1]) & 0xFFFFu) << 16);
-      fold_split_silu<ACT, HILO>(p, routed, p0, kb, ke);
+      fold_split_silu<ACT, HILO>(p, routed, p0, kb, ke, (int)(threadIdx.x & 127));
       __syncthreads();  // h of the item's rows and k-range is in place
     }
   }
@@ -307,16 +343,23 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[q][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  static_assert(HV == 1 || EPI == EPI_SILU_MUL, "two halves: gate|up, whose slabs are all active");
   if (active && nsteps > 0) {
     u32x4 xb[S][2];
     u32x4 xl[HILO ? S : 1][2];
     u32x4 mxs[MX ? S : 1];
-    // stage s <- k-step `step` (clamped: steps past the end reload the last)
-    auto issue = [&](int s, int step) {
+    // stage s <- k-step `step` (clamped: steps past the end reload the last);
+    // tok (a std::bool_constant): also the wave's token rows (and MX scales),
+    // which an empty half does not load
+    auto issue = [&](int s, int step, auto tok) {
       const int sc = min(step, nsteps - 1);
       const char* src = wbase + (int64_t)sc * kstep_bytes;
 #pragma unroll
-      for (int j = 0; j < RPL; ++j) dma16(src + j * wrow_bytes, ring + (s * RPL + j) * WAVE);
+      for (int jw = 0; jw < RPW; ++jw) {
+        const int j = jw * HV + half;
+        dma16(src + j * wrow_bytes, ring + (s * RPL + j) * WAVE);
+      }
+      if constexpr (!decltype(tok)::value) return;
       const int64_t kk = (int64_t)(kb + sc * KSTEP + XK * lg) * ASZ;
       xb[s][0] = ld16(arow[0] + kk);
       xb[s][1] = ld16(arow[1] + kk);
@@ -431,20 +474,58 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
         }
       }
     };
+    const std::true_type tok;
+    // The first S-1 stages are loaded up front.  Step j: this wave's share
+    // of stage j % S has landed once at most the S-2 stages issued after it
+    // are in flight (steps up to j+S-2); after the barrier every share has,
+    // and every wave is done reading the stage of step j-1 (at j = 0: the
+    // stage not yet loaded), which is loaded with step j+S-1 before stage j
+    // is computed.  Every wave runs every barrier; live_c (a bool_constant):
+    // the half has routed rows (else the wave only loads its weight share,
+    // so its wait counts those alone).
+    auto loop2 = [&](auto q1_c, auto live_c) {
+      constexpr bool LIVE = decltype(live_c)::value;
+      constexpr int P = LIVE ? PER : RPW;
 #pragma unroll
-    for (int s = 0; s < S; ++s) issue(s, s);
-    auto main_loop = [&](auto q1_c) {
+      for (int s = 0; s < S - 1; ++s) issue(s, s, live_c);
       for (int it = 0; it < nsteps; it += S) {
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-          // stage s complete: only the S-1 later stages may still be in flight
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * PER));
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * P));
+          __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
-          if (it + s < nsteps) compute(s, q1_c);
+          issue((s + S - 1) % S, it + s + S - 1, live_c);
           __builtin_amdgcn_sched_barrier(0);
-          issue(s, it + s + S);
+          if constexpr (LIVE) {
+            if (it + s < nsteps) compute(s, q1_c);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
+    };
+    if constexpr (HV == 1) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) issue(s, s, tok);
+    }
+    auto main_loop = [&](auto q1_c) {
+      if constexpr (HV == 1) {
+        for (int it = 0; it < nsteps; it += S) {
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            // stage s complete: only the S-1 later stages may still be in flight
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * PER));
+            __builtin_amdgcn_sched_barrier(0);
+            if (it + s < nsteps) compute(s, q1_c);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(s, it + s + S, tok);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      } else {
+        if (live)
+          loop2(q1_c, std::true_type{});
+        else
+          loop2(q1_c, std::false_type{});
       }
     };
     // MXFP4 gains from one loop per case (its many conversions leave no issue
@@ -510,9 +591,14 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
     // wave 0 (gate) finishes row group 0 and wave 1 (up) row group 1; each
     // hands the other the accumulators of the group it does not finish
     // (selects, not indexing by the wave number, keep acc in registers)
-    f32x4* xch = reinterpret_cast<f32x4*>(lds);  // [2][CPL][WAVE]
+    f32x4* xch = reinterpret_cast<f32x4*>(lds) + half * 2 * CPL * WAVE;  // [HV][2][CPL][WAVE]
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) xch[(slab * CPL + c) * WAVE + lane] = slab ? acc[0][c] : acc[1][c];
+    for (int c = 0; c < CPL; ++c) {
+      // selects of values (copies), not of the two array elements: a select
+      // of element addresses made the compiler keep acc in private memory
+      const f32x4 a0 = acc[0][c], a1 = acc[1][c];
+      xch[(slab * CPL + c) * WAVE + lane] = slab ? a0 : a1;
+    }
     __syncthreads();
     const int keep = slab;
     if (!rvalid[keep]) return;
@@ -520,7 +606,8 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
     float h[NV];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const f32x4 mine = slab ? acc[1][c] : acc[0][c];
+      const f32x4 a0 = acc[0][c], a1 = acc[1][c];
+      const f32x4 mine = slab ? a1 : a0;
       const f32x4 other = xch[((1 - slab) * CPL + c) * WAVE + lane];
       const f32x4 g = slab ? other : mine;
       const f32x4 u = slab ? mine : other;
@@ -560,17 +647,20 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
 // front per expert group and no partly filled last round.  Items are numbered
 // n-tile fastest, so the blocks in use (a prefix of the m-blocks) make a
 // prefix of the items.
-template <int ACT, int WT, int EPI, bool HILO>
-__global__ __launch_bounds__(128) void k_expert_stream(const StreamGemmArgs p) {
-  // ring[wave][stage][row][lane]; after an item's main loop the same memory
+template <int ACT, int WT, int EPI, bool HILO, int HV>
+__global__ __launch_bounds__(128 * HV) void k_expert_stream(const StreamGemmArgs p) {
+  // ring[slab][stage][row][lane]; after an item's main loop the same memory
   // holds its epilogue exchange
-  __shared__ u32x4 lds[2 * stages_of<WT>() * DTr<WT>::RPL * WAVE];
+  constexpr int RING = 2 * stages_of<WT, HV>() * DTr<WT>::RPL * WAVE;
+  static_assert(EPI != EPI_SILU_MUL || HV * 2 * DTr<WT>::CPL * WAVE <= RING,
+                "the epilogue exchange fits the ring");
+  __shared__ u32x4 lds[RING];
   int blocks = p.num_mblocks;
   if (p.padded_rows != nullptr) blocks = min(blocks, *p.padded_rows / STREAM_BM);
   const int items = blocks * p.n_tiles * p.ksplit;
   for (int i = blockIdx.x; i < items; i += gridDim.x) {
     __syncthreads();  // the previous item's epilogue is done with the ring
-    stream_item<ACT, WT, EPI, HILO>(p, i, lds);
+    stream_item<ACT, WT, EPI, HILO, HV>(p, i, lds);
   }
 }
 
@@ -587,24 +677,45 @@ int stream_kstep(int w_dtype) {
   return (w_dtype == W_F32) ? DTr<W_F32>::KSTEP : DTr<W_BF16>::KSTEP;
 }
 
+template <int ACT, int WT, int EPI, int HV>
+static hipError_t launch_hv(const StreamGemmArgs& a, int64_t grid, hipStream_t st) {
+  if constexpr (ACT == ACT_BF16 && WT != W_F32 && EPI == EPI_STORE) {
+    if (a.a_lo != nullptr) {
+      hipLaunchKernelGGL((k_expert_stream<ACT, WT, EPI, true, HV>), dim3((unsigned)grid),
+                         dim3(128 * HV), 0, st, a);
+      return hipGetLastError();
+    }
+  } else {
+    if (a.a_lo != nullptr) return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL((k_expert_stream<ACT, WT, EPI, false, HV>), dim3((unsigned)grid),
+                     dim3(128 * HV), 0, st, a);
+  return hipGetLastError();
+}
+
+// two-half blocks for fp8 weights only (with the MX formats' scale loads in
+// the ring the compiler drains every load before their use)
+template <int WT>
+constexpr bool has_halves() {
+  return WT == W_FP8;
+}
+
 template <int ACT, int WT, int EPI>
 static hipError_t launch_one(const StreamGemmArgs& a, hipStream_t st) {
   const int64_t items = (int64_t)a.num_mblocks * a.n_tiles * a.ksplit;
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFF || a.wgs < 0) return hipErrorInvalidValue;
   const int64_t grid = a.wgs > 0 ? std::min<int64_t>(a.wgs, items) : items;
-  if constexpr (ACT == ACT_BF16 && WT != W_F32 && EPI == EPI_STORE) {
-    if (a.a_lo != nullptr) {
-      hipLaunchKernelGGL((k_expert_stream<ACT, WT, EPI, true>), dim3((unsigned)grid), dim3(128),
-                         0, st, a);
-      return hipGetLastError();
-    }
-  } else {
-    if (a.a_lo != nullptr) return hipErrorInvalidValue;
+  if (a.halves == 2) {
+    // gate|up only (every slab of its n-tiles lies inside the output, so
+    // every wave runs the k-loop's barriers)
+    if (a.expert_offsets == nullptr || a.block_expert == nullptr) return hipErrorInvalidValue;
+    if constexpr (ACT == ACT_BF16 && has_halves<WT>() && EPI == EPI_SILU_MUL)
+      return launch_hv<ACT, WT, EPI, 2>(a, grid, st);
+    return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((k_expert_stream<ACT, WT, EPI, false>), dim3((unsigned)grid), dim3(128), 0,
-                     st, a);
-  return hipGetLastError();
+  if (a.halves > 2) return hipErrorInvalidValue;
+  return launch_hv<ACT, WT, EPI, 1>(a, grid, st);
 }
 
 hipError_t launch_stream_gemm(int act, int wdt, int epi, const StreamGemmArgs& a, hipStream_t st) {

@@ -452,6 +452,15 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   // the tiled GEMM's half tiles pair two 256-column tiles, so experts are
   // padded to 128 rows when both GEMMs have an even number of column tiles
   const bool half_rows = tiled && (dff / (TILED_BN / 2)) % 2 == 0 && (d / TILED_BN) % 2 == 0;
+  // fp8 weights on the weight-streaming GEMM, once the batch averages
+  // STREAM_HALVES_MIN entries per expert: the gate|up GEMM applies one weight
+  // stream to a pair of an expert's 32-row blocks, so a skewed expert
+  // streams its weights once per 64 rows (E=256 top-8 T=128, Zipf 1.2: 77
+  // blocks in 63 pairs and singles; gate|up 447 -> 332 us).  The down GEMM
+  // (short K: one-block items overlap better) keeps one block per item
+  // (pairs: 202 -> 282 us)
+  const bool halves2 = !tiled && act == ACT_BF16 && wdt == W_FP8 &&
+                       n >= (int64_t)STREAM_HALVES_MIN * E;
   const int bm = tiled ? (half_rows ? TILED_BM / 2 : TILED_BM) : STREAM_BM;
   const int64_t cap = moe_align_capacity(T, E, k, bm);
   const int64_t nblocks = cap / bm;
@@ -621,6 +630,8 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g.ksplit = gu_split;
   g.kchunk = gu_chunk;
   g.wgs = gu_wgs;
+  g.halves = halves2 ? 2 : 1;
+  g.expert_offsets = offs;
   g.partial = gu_part;
   g.partial_ld = 2 * (int64_t)dff;
   g.partial_split_stride = cap * 2 * dff;
@@ -662,6 +673,7 @@ int moe_forward_traced(const moe_layer* L, const void* x, int T, void* out, void
   g2.ksplit = dn_split;
   g2.kchunk = dn_chunk;
   g2.wgs = dn_wgs;
+  g2.halves = 1;
   g2.partial = static_cast<float*>(y);
   g2.partial_ld = d;
   g2.partial_split_stride = cap * d;

@@ -71,6 +71,10 @@ struct StreamGemmArgs {
   int64_t out_split_stride;  // router: elements between split planes
   int wgs;                // stream GEMM: workgroups, each looping over items
                           //   g, g + wgs, ...; 0 = one workgroup per item
+  int halves;             // stream GEMM: 32-row blocks per item (1, or 2: an item
+                          //   applies one weight stream to a pair of its expert's
+                          //   blocks, and needs expert_offsets)
+  const int32_t* expert_offsets;  // halves == 2: the alignment's padded offsets [E + 1]
   const int32_t* tile_rows;    // tiled GEMM: [rows][2] = {first slot, expert | routed
                                //   slots << 16}, full rows (256 slots) first, then half
                                //   rows (128 slots); routed slots are the row's first ones
@@ -84,6 +88,9 @@ int device_cus();
 
 // Rows per m-block of the stream GEMM (two 16-row MFMA column groups).
 constexpr int STREAM_BM = 32;
+// routed entries per expert (on average) from which fp8 weights take 64-row
+// stream blocks
+constexpr int STREAM_HALVES_MIN = 4;
 
 // Output columns covered by one n-tile of the stream GEMM.
 int stream_tile_cols(int w_dtype, int epi);

@@ -85,6 +85,14 @@ SMALL = [
     (4, 2, 256, 512, "bf16", "fp8", 400, None),
     (16, 4, 512, 256, "bf16", "fp8", 700, 1.0),      # skewed, ragged blocks
     (2, 1, 768, 256, "bf16", "fp8", 600, None),      # 24 k-steps of gate|up
+    # fp8 on the stream GEMM with >= 4 entries per expert: the gate|up GEMM
+    # applies one weight stream to pairs of an expert's 32-row blocks
+    # (skewed: heavy experts fill pairs, light ones leave the second empty;
+    # odd block counts end in a single)
+    (16, 4, 512, 256, "bf16", "fp8", 100, 1.2),
+    (8, 2, 1024, 512, "bf16", "fp8", 150, None),
+    (64, 8, 512, 512, "bf16", "fp8", 300, 1.0),
+    (4, 2, 2048, 256, "bf16", "fp8", 16, None),      # k-split gate|up (folded) and down
     # MXFP4 experts (E2M1 codes, an E8M0 scale per 32 k): always the stream GEMM
     (8, 2, 256, 256, "bf16", "mxfp4", 5, None),
     (32, 8, 512, 256, "bf16", "mxfp4", 40, 1.2),
