@@ -227,8 +227,8 @@ __device__ __forceinline__ void fold_split_silu(const StreamGemmArgs& p, uint32_
 // HV = 1: one 32-row block per item, two waves (one per slab), each wave
 // with a load ring of its own and no workgroup barrier in the k-loop.  HV = 2
 // (gate|up with fp8 weights): a pair of consecutive blocks of one expert per
-// item, four waves; wave (slab, half) applies its slab's weights to the rows
-// of block `half` of the pair.  The two waves of a slab share one ring: each
+// item, four waves; wave (slab, blk) applies its slab's weights to the rows
+// of block `blk` of the pair.  The two waves of a slab share one ring: each
 // issues half of every stage's weight rows (the same lane addresses either
 // would use), and one workgroup barrier per k-step, after each wave's own
 // vmcnt wait, publishes the landed stage and retires the stage read in the
@@ -256,11 +256,13 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
   // with HILO) (+ the MX scales)
   constexpr int PER = RPW + (HILO ? 4 : 2) + (MX ? 1 : 0);
   static_assert((S - 1) * PER <= 63, "vmcnt field");
+  // (a loop whose second row group is known empty issues one token load
+  // fewer per stage, two with HILO, and counts accordingly)
   static_assert(HV == 1 || S >= 3, "a shared ring keeps a stage in flight past the barrier");
 
   const int lane = threadIdx.x & 63;
   const int slab = HV == 1 ? (int)(threadIdx.x >> 6) : (int)(threadIdx.x >> 6) & 1;
-  const int half = HV == 1 ? 0 : (int)(threadIdx.x >> 7);
+  const int blk = HV == 1 ? 0 : (int)(threadIdx.x >> 7);  // block of the pair
   const int li = lane & 15;  // MFMA column within a 16-group (token row)
   const int lg = lane >> 4;  // k group
 
@@ -277,9 +279,9 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
   if constexpr (HV == 2) {
     const int first = p.expert_offsets[e] / STREAM_BM;
     if ((mb - first) & 1) return;  // whole workgroup
-    half_ok = half == 0 || mb + 1 < p.expert_offsets[e + 1] / STREAM_BM;
+    half_ok = blk == 0 || mb + 1 < p.expert_offsets[e + 1] / STREAM_BM;
   }
-  const int p0 = (mb + half) * STREAM_BM;
+  const int p0 = (mb + blk) * STREAM_BM;
 
   // -------------------------------------------------------- token rows
   const char* arow[2];
@@ -326,7 +328,13 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
   const char* sbase = MX ? reinterpret_cast<const char*>(p.scale) + (int64_t)e * p.scale_estride +
                                (int64_t)(kb / KSTEP) * p.w_ld + wcol
                          : nullptr;
-  u32x4* ring = lds + slab * S * RPL * WAVE;
+  // MX weights: the stage's E8M0 scales come through the ring as one more
+  // row (with HV = 2 both waves of a live pair load the same bytes to the
+  // same place); register-loaded scales made the compiler drain every load
+  // (vmcnt(0)) before their use once per pass of the unrolled loop
+  constexpr bool MXL = MX;
+  constexpr int RPR = RPL + (MXL ? 1 : 0);  // ring rows per stage
+  u32x4* ring = lds + slab * S * RPR * WAVE;
   if constexpr (EPI == EPI_STORE) {
     if (p.a_part != nullptr) {  // uniform
       // lanes 0-15 hold rows 0-15 (q = 0) and 16-31 (q = 1)
@@ -347,34 +355,40 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
   if (active && nsteps > 0) {
     u32x4 xb[S][2];
     u32x4 xl[HILO ? S : 1][2];
-    u32x4 mxs[MX ? S : 1];
     // stage s <- k-step `step` (clamped: steps past the end reload the last);
     // tok (a std::bool_constant): also the wave's token rows (and MX scales),
-    // which an empty half does not load
-    auto issue = [&](int s, int step, auto tok) {
+    // which an empty half does not load; q1 (std::false_type: the second
+    // 16-row group is known empty): not its token row — the compiler drops
+    // that load anyway once nothing reads it, and the wait counts must then
+    // not count it
+    auto issue = [&](int s, int step, auto tok, auto q1) {
       const int sc = min(step, nsteps - 1);
       const char* src = wbase + (int64_t)sc * kstep_bytes;
 #pragma unroll
       for (int jw = 0; jw < RPW; ++jw) {
-        const int j = jw * HV + half;
-        dma16(src + j * wrow_bytes, ring + (s * RPL + j) * WAVE);
+        const int j = jw * HV + blk;
+        dma16(src + j * wrow_bytes, ring + (s * RPR + j) * WAVE);
       }
       if constexpr (!decltype(tok)::value) return;
       const int64_t kk = (int64_t)(kb + sc * KSTEP + XK * lg) * ASZ;
+      constexpr bool Q1 = !std::is_same_v<decltype(q1), std::false_type>;
       xb[s][0] = ld16(arow[0] + kk);
-      xb[s][1] = ld16(arow[1] + kk);
+      if constexpr (Q1) xb[s][1] = ld16(arow[1] + kk);
       if constexpr (HILO) {
         xl[s][0] = ld16(alrow[0] + kk);
-        xl[s][1] = ld16(alrow[1] + kk);
+        if constexpr (Q1) xl[s][1] = ld16(alrow[1] + kk);
       }
-      if constexpr (MX) mxs[s] = ld16(sbase + (int64_t)sc * p.w_ld);
+      if constexpr (MXL) dma16(sbase + (int64_t)sc * p.w_ld, ring + (s * RPR + RPL) * WAVE);
     };
     // q1: the block's second 16-row group holds routed rows — a runtime bool
     // (a branch per MFMA) or, for MXFP4, std::true_type/false_type (folded)
     auto compute = [&](int s, auto q1) {
       u32x4 raw[RPL];
 #pragma unroll
-      for (int j = 0; j < RPL; ++j) raw[j] = ring[(s * RPL + j) * WAVE + lane];
+      for (int j = 0; j < RPL; ++j) raw[j] = ring[(s * RPR + j) * WAVE + lane];
+      // MX: the lane's 16 E8M0 scale bytes of the k-step
+      u32x4 msc = {0u, 0u, 0u, 0u};
+      if constexpr (MXL) msc = ring[(s * RPR + RPL) * WAVE + lane];
       const u32x4 z = {0u, 0u, 0u, 0u};
       const u32x4 x0 = rvalid[0] ? xb[s][0] : z;
       const u32x4 x1 = rvalid[1] ? xb[s][1] : z;
@@ -413,7 +427,7 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
         // E8M0 byte e of column c -> the fp32 2^(e-127) (exponent field e,
         // zero mantissa)
         auto scl_of = [&](int c) {
-          return __uint_as_float(((mxs[s][c >> 2] >> (8 * (c & 3))) & 0xFFu) << 23);
+          return __uint_as_float(((msc[c >> 2] >> (8 * (c & 3))) & 0xFFu) << 23);
         };
         if constexpr (!HILO) {
           // one fragment at a time (fewest live registers)
@@ -461,7 +475,7 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
               // as the fp32 2^(e-127) (exponent field e, zero mantissa)
               float scl[4] = {1.0f, 1.0f, 1.0f, 1.0f};
               if constexpr (WT == W_MXFP8) {
-                const uint32_t sw = mxs[s][2 * half + w];
+                const uint32_t sw = msc[2 * half + w];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) scl[c] = __uint_as_float(((sw >> (8 * c)) & 0xFFu) << 23);
               }
@@ -485,16 +499,17 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
     // so its wait counts those alone).
     auto loop2 = [&](auto q1_c, auto live_c) {
       constexpr bool LIVE = decltype(live_c)::value;
-      constexpr int P = LIVE ? PER : RPW;
+      constexpr int P =
+          LIVE ? PER - (std::is_same_v<decltype(q1_c), std::false_type> ? (HILO ? 2 : 1) : 0) : RPW;
 #pragma unroll
-      for (int s = 0; s < S - 1; ++s) issue(s, s, live_c);
+      for (int s = 0; s < S - 1; ++s) issue(s, s, live_c, q1_c);
       for (int it = 0; it < nsteps; it += S) {
 #pragma unroll
         for (int s = 0; s < S; ++s) {
           __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * P));
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
-          issue((s + S - 1) % S, it + s + S - 1, live_c);
+          issue((s + S - 1) % S, it + s + S - 1, live_c, q1_c);
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (LIVE) {
             if (it + s < nsteps) compute(s, q1_c);
@@ -503,21 +518,23 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
         }
       }
     };
-    if constexpr (HV == 1) {
-#pragma unroll
-      for (int s = 0; s < S; ++s) issue(s, s, tok);
-    }
     auto main_loop = [&](auto q1_c) {
       if constexpr (HV == 1) {
+        constexpr int P =
+            PER - (std::is_same_v<decltype(q1_c), std::false_type> ? (HILO ? 2 : 1) : 0);
+        // the first S stages, with the loop's own loads (a load the loop
+        // never reads would have to be drained before its register is reused)
+#pragma unroll
+        for (int s = 0; s < S; ++s) issue(s, s, tok, q1_c);
         for (int it = 0; it < nsteps; it += S) {
 #pragma unroll
           for (int s = 0; s < S; ++s) {
             // stage s complete: only the S-1 later stages may still be in flight
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * PER));
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * P));
             __builtin_amdgcn_sched_barrier(0);
             if (it + s < nsteps) compute(s, q1_c);
             __builtin_amdgcn_sched_barrier(0);
-            issue(s, it + s + S, tok);
+            issue(s, it + s + S, tok, q1_c);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -591,7 +608,7 @@ __device__ __forceinline__ void stream_item(const StreamGemmArgs& p, int id, u32
     // wave 0 (gate) finishes row group 0 and wave 1 (up) row group 1; each
     // hands the other the accumulators of the group it does not finish
     // (selects, not indexing by the wave number, keep acc in registers)
-    f32x4* xch = reinterpret_cast<f32x4*>(lds) + half * 2 * CPL * WAVE;  // [HV][2][CPL][WAVE]
+    f32x4* xch = reinterpret_cast<f32x4*>(lds) + blk * 2 * CPL * WAVE;  // [HV][2][CPL][WAVE]
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       // selects of values (copies), not of the two array elements: a select
@@ -651,7 +668,8 @@ template <int ACT, int WT, int EPI, bool HILO, int HV>
 __global__ __launch_bounds__(128 * HV) void k_expert_stream(const StreamGemmArgs p) {
   // ring[slab][stage][row][lane]; after an item's main loop the same memory
   // holds its epilogue exchange
-  constexpr int RING = 2 * stages_of<WT, HV>() * DTr<WT>::RPL * WAVE;
+  constexpr bool MXL = WT == W_FP4 || WT == W_MXFP8;
+  constexpr int RING = 2 * stages_of<WT, HV>() * (DTr<WT>::RPL + (MXL ? 1 : 0)) * WAVE;
   static_assert(EPI != EPI_SILU_MUL || HV * 2 * DTr<WT>::CPL * WAVE <= RING,
                 "the epilogue exchange fits the ring");
   __shared__ u32x4 lds[RING];
@@ -693,8 +711,8 @@ static hipError_t launch_hv(const StreamGemmArgs& a, int64_t grid, hipStream_t s
   return hipGetLastError();
 }
 
-// two-half blocks for fp8 weights only (with the MX formats' scale loads in
-// the ring the compiler drains every load before their use)
+// block pairs for fp8 weights (MXFP8 and MXFP4 pairs measured slower at
+// E=256 top-8 T=128: gate|up 484 -> 504 and 264 -> 341 us)
 template <int WT>
 constexpr bool has_halves() {
   return WT == W_FP8;

@@ -98,12 +98,16 @@ SMALL = [
     (32, 8, 512, 256, "bf16", "mxfp4", 40, 1.2),
     (4, 2, 256, 512, "bf16", "mxfp4", 300, None),    # many rows per expert
     (16, 4, 768, 256, "bf16", "mxfp4", 257, 1.0),    # 24 scale blocks along d
+    (16, 4, 512, 512, "bf16", "mxfp4", 100, 1.2),    # heavy experts, many blocks
+    (4, 2, 2048, 256, "bf16", "mxfp4", 16, None),    # k-split gate|up
     (1024, 4, 256, 256, "bf16", "bf16", 300, None),  # MOE_MAX_EXPERTS experts
     # MXFP8 experts (e4m3fn codes, an E8M0 scale per 32 k): the stream GEMM
     (8, 2, 256, 256, "bf16", "mxfp8", 5, None),
     (32, 8, 512, 256, "bf16", "mxfp8", 40, 1.2),
     (4, 2, 256, 512, "bf16", "mxfp8", 300, None),    # many rows per expert
     (16, 4, 768, 256, "bf16", "mxfp8", 257, 1.0),    # 24 scale blocks along d
+    (16, 4, 512, 512, "bf16", "mxfp8", 100, 1.2),    # heavy experts, many blocks
+    (4, 2, 2048, 256, "bf16", "mxfp8", 16, None),    # k-split gate|up
 ]
 
 
