@@ -23,11 +23,15 @@ CASES = [
      2),
     (LayerShape(304, "graph-fold-fp8", E=16, k=4, d=1024, d_ff=256, act="bf16", wdt="fp8",
                 seed=10), 2),
+    # fp8 with >= 4 entries per expert: the gate|up GEMM's block pairs
+    (LayerShape(305, "graph-pairs-fp8", E=16, k=4, d=512, d_ff=256, act="bf16", wdt="fp8",
+                seed=11), 200),
 ]
 
 
 @pytest.mark.parametrize("sh,T", CASES,
-                         ids=["decode-bf16", "tiled-bf16", "mxfp4", "fold-bf16", "fold-fp8"])
+                         ids=["decode-bf16", "tiled-bf16", "mxfp4", "fold-bf16", "fold-fp8",
+                              "pairs-fp8"])
 def test_graph_replays_match_eager(sh, T):
     print(f"graph replay {sh.name} T={T}", flush=True)
     layer = make_layer(sh, T, "cuda")

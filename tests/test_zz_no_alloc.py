@@ -24,6 +24,9 @@ CASES = [
                 seed=44), 1200, 300),
     (LayerShape(704, "noalloc-f32", E=8, k=2, d=128, d_ff=256, act="f32", wdt="f32",
                 seed=45), 16, 5),
+    # fp8 gate|up block pairs (>= 4 entries per expert in both calls)
+    (LayerShape(705, "noalloc-pairs-fp8", E=16, k=4, d=512, d_ff=512, act="bf16", wdt="fp8",
+                seed=46), 200, 20),
 ]
 
 
