@@ -93,6 +93,12 @@ SMALL = [
     (8, 2, 1024, 512, "bf16", "fp8", 150, None),
     (64, 8, 512, 512, "bf16", "fp8", 300, 1.0),
     (4, 2, 2048, 256, "bf16", "fp8", 16, None),      # k-split gate|up (folded) and down
+    # either side of the regime switches: 4 entries per expert (pairs from
+    # T*k = 64 at E=16) and 64 per expert (the tiled GEMM from T*k = 256 at E=4)
+    (16, 4, 512, 256, "bf16", "fp8", 15, 1.2),
+    (16, 4, 512, 256, "bf16", "fp8", 16, 1.2),
+    (4, 2, 256, 256, "bf16", "fp8", 127, None),
+    (4, 2, 256, 256, "bf16", "fp8", 128, None),
     # MXFP4 experts (E2M1 codes, an E8M0 scale per 32 k): always the stream GEMM
     (8, 2, 256, 256, "bf16", "mxfp4", 5, None),
     (32, 8, 512, 256, "bf16", "mxfp4", 40, 1.2),
